@@ -1,0 +1,88 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that the pins catch each one.
+
+Each mutant replaces one internal step of ``oracle.fp64`` via monkeypatch; the pins in
+``test_oracle_pins`` are then run against the mutant and at least one must fail.
+"""
+import numpy as np
+import pytest
+
+from oracle import fp64
+from tests import test_oracle_pins as pins
+
+
+def _terms_transposed_shift(hb, W):
+    z = hb @ W.T
+    M = z.max(axis=1)
+    S = np.exp(z - M[:, None]).sum(axis=1)
+    lse = M + np.log(S)
+    return z, lse, z - lse[:, None] + 1e-3        # off by a constant
+
+
+def _terms_no_max(hb, W):
+    z = hb @ W.T
+    M = z.max(axis=1)
+    S = np.exp(z - M[:, None]).sum(axis=1)
+    lse = np.log(S)                                # dropped the max term
+    return z, lse, z - lse[:, None]
+
+
+def _gather_next(logp, yb, V):
+    out = np.zeros(logp.shape[0])
+    valid = (yb >= 0) & (yb < V)
+    r = np.nonzero(valid)[0]
+    out[r] = logp[r, (yb[r] + 1) % V]              # wrong index
+    return out
+
+
+def _dz_sign(logp, yb, gb, V):
+    dz = np.exp(logp) * gb[:, None]                # wrong sign of the softmax term
+    valid = (yb >= 0) & (yb < V)
+    r = np.nonzero(valid)[0]
+    dz[r, yb[r]] += gb[r]
+    return dz
+
+
+def _dz_no_onehot(logp, yb, gb, V):
+    return -np.exp(logp) * gb[:, None]             # dropped the label term
+
+
+PIN_SETS = {
+    "forward": [
+        lambda: pins.test_fp64_matches_brute_forward(5, 24, 7),
+        pins.test_probabilities_sum_to_one_and_lse_identical,
+        lambda: pins.test_uniform_logits_give_minus_log_v(4096, -8.317766166719343),
+        pins.test_two_vocab_entries_softplus,
+        pins.test_one_hot_design_exact_logits,
+    ],
+    "backward": [
+        lambda: pins.test_fp64_matches_brute_backward(4, 12, 5),
+        pins.test_backward_matches_central_differences,
+        pins.test_backward_zero_hidden_closed_form,
+        pins.test_grad_weight_column_sums,
+    ],
+}
+
+
+def _some_pin_fails(kind):
+    for fn in PIN_SETS[kind]:
+        try:
+            fn()
+        except AssertionError:
+            return True
+    return False
+
+
+@pytest.mark.parametrize("name,target,mutant,kind", [
+    ("logp offset", "_block_softmax_terms", _terms_transposed_shift, "forward"),
+    ("lse without max", "_block_softmax_terms", _terms_no_max, "forward"),
+    ("gather wrong index", "_gather_label", _gather_next, "forward"),
+    ("dz sign", "_dz_block", _dz_sign, "backward"),
+    ("dz without onehot", "_dz_block", _dz_no_onehot, "backward"),
+])
+def test_pins_catch_planted_mistake(monkeypatch, name, target, mutant, kind):
+    monkeypatch.setattr(fp64, target, mutant)
+    assert _some_pin_fails(kind), f"no pin caught the planted mistake: {name}"
+
+
+def test_unmutated_oracle_passes_all_pins():
+    assert not _some_pin_fails("forward") and not _some_pin_fails("backward")

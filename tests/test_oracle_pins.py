@@ -1,0 +1,233 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle itself.
+
+The pages print no log-prob or entropy values for any input, so the oracle is pinned by
+mathematics: an independent scalar implementation with correctly rounded sums, closed forms,
+invariants, special cases and finite differences.  Each pin is chosen so that a plausible slip
+(a dropped term, a sign, an index, a transposed operand) breaks at least one of them.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import brute, fp64
+
+
+def _bf16(x):
+    return torch.as_tensor(x, dtype=torch.float32).to(torch.bfloat16)
+
+
+def _rand_case(T, H, V, seed, hstd=1.0, wstd=0.3):
+    h = synth.hidden(T, H, seed, hstd)
+    W = synth.weight(V, H, seed, wstd)
+    y = synth.labels(T, V, seed)
+    return h, W, y
+
+
+# --------------------------------------------------------------------------------------------
+# fp64 oracle vs the scalar fsum oracle (independent implementations)
+# --------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,H,V", [(5, 24, 7), (3, 40, 1), (4, 8, 2), (6, 16, 11)])
+def test_fp64_matches_brute_forward(T, H, V):
+    h, W, y = _rand_case(T, H, V, seed=3)
+    y = y.clone()
+    if T >= 4:
+        y[1] = -1      # out of range: logprob 0
+        y[2] = V       # out of range
+    ref_lp, ref_ent, ref_lse = brute.forward(h, W, y)
+    out = fp64.forward(h, W, y)
+    np.testing.assert_allclose(out["logprob"], ref_lp, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(out["entropy"], ref_ent, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(out["lse"], ref_lse, rtol=0, atol=1e-12)
+    if T >= 4:
+        assert out["logprob"][1] == 0.0 and out["logprob"][2] == 0.0
+
+
+def test_fp64_matches_brute_nonsquare_transposes():
+    # H != V != T so that any transposed operand changes shapes or values.
+    h, W, y = _rand_case(3, 10, 6, seed=11)
+    lp, ent, lse = brute.forward(h, W, y)
+    out = fp64.forward(h, W, y)
+    np.testing.assert_allclose(out["logprob"], lp, atol=1e-12, rtol=0)
+    np.testing.assert_allclose(out["entropy"], ent, atol=1e-12, rtol=0)
+
+
+@pytest.mark.parametrize("T,H,V", [(4, 12, 5), (3, 8, 9)])
+def test_fp64_matches_brute_backward(T, H, V):
+    h, W, y = _rand_case(T, H, V, seed=5)
+    y = y.clone()
+    y[0] = -100        # out-of-range label: no onehot term
+    g = synth.upstream_grad(T, 5)
+    gh_ref, gW_ref = brute.backward(h, W, y, g)
+    gh, gW = fp64.backward(h, W, y, g)
+    np.testing.assert_allclose(gh, gh_ref, atol=1e-12, rtol=0)
+    np.testing.assert_allclose(gW, gW_ref, atol=1e-12, rtol=0)
+    # sampled-row helpers agree with the full backward
+    np.testing.assert_allclose(fp64.grad_hidden_rows(h, W, y, g, [2, 0]), gh[[2, 0]], atol=1e-13, rtol=0)
+    np.testing.assert_allclose(fp64.grad_weight_rows(h, W, y, g, [V - 1, 1]), gW[[V - 1, 1]], atol=1e-13, rtol=0)
+
+
+# --------------------------------------------------------------------------------------------
+# closed forms and invariants of the log-softmax / gather
+# --------------------------------------------------------------------------------------------
+
+def test_probabilities_sum_to_one_and_lse_identical():
+    V, H = 13, 32
+    h1, W, _ = _rand_case(1, H, V, seed=7)
+    h = h1.repeat(V, 1)
+    y = torch.arange(V, dtype=torch.int32)
+    out = fp64.forward(h, W, y)
+    assert abs(math.fsum(np.exp(out["logprob"])) - 1.0) < 1e-12
+    assert np.all(out["lse"] == out["lse"][0])
+    assert np.all(out["entropy"] == out["entropy"][0])
+    # gather index: logprob at label j equals z_j - lse
+    z = fp64.to_f64(h1) @ fp64.to_f64(W).T
+    np.testing.assert_allclose(out["logprob"], z[0] - out["lse"][0], atol=1e-13, rtol=0)
+
+
+@pytest.mark.parametrize("V,expected", [(4096, -8.317766166719343), (152064, -11.932056763842207)])
+def test_uniform_logits_give_minus_log_v(V, expected):
+    # ln 4096 = 12 ln 2; ln 152064 = 8 ln 2 + ln 594 (594 = 2 * 3^3 * 11).
+    assert abs(expected + (8 * math.log(2) + math.log(594) if V == 152064 else 12 * math.log(2))) < 1e-12
+    H = 8
+    h = torch.zeros((3, H), dtype=torch.bfloat16)          # h = 0 -> all logits 0
+    W = synth.weight(V, H, 1, 0.02)
+    y = torch.tensor([0, V // 2, V - 1], dtype=torch.int32)
+    out = fp64.forward(h, W, y)
+    np.testing.assert_allclose(out["logprob"], expected, atol=1e-12, rtol=0)
+    np.testing.assert_allclose(out["entropy"], -expected, atol=1e-12, rtol=0)
+    # W = 0 gives the same
+    out2 = fp64.forward(synth.hidden(3, H, 2), torch.zeros((V, H), dtype=torch.bfloat16), y)
+    np.testing.assert_allclose(out2["logprob"], expected, atol=1e-12, rtol=0)
+
+
+def test_single_vocab_entry():
+    h, W, _ = _rand_case(4, 16, 1, seed=9)
+    out = fp64.forward(h, W, torch.zeros(4, dtype=torch.int32))
+    assert np.all(out["logprob"] == 0.0)
+    assert np.all(np.abs(out["entropy"]) <= 1e-15)
+
+
+def test_two_vocab_entries_softplus():
+    # bf16-exact integers: z = h @ W^T is known by hand.
+    h = _bf16([[1.0, 2.0], [3.0, -1.0], [0.5, 0.25]])
+    W = _bf16([[3.0, 0.0], [0.0, 1.0]])
+    z = [[3.0, 2.0], [9.0, -1.0], [1.5, 0.25]]
+    y = torch.tensor([0, 1, 1], dtype=torch.int32)
+    out = fp64.forward(h, W, y)
+    for t in range(3):
+        zy, zo = z[t][y[t]], z[t][1 - y[t]]
+        lp = -math.log1p(math.exp(zo - zy))
+        p = 1.0 / (1.0 + math.exp(z[t][1] - z[t][0]))
+        ent = -(p * math.log(p) + (1 - p) * math.log1p(-p))
+        assert abs(out["logprob"][t] - lp) < 1e-13
+        assert abs(out["entropy"][t] - ent) < 1e-13
+
+
+def test_shift_invariance():
+    T, H, V, c = 6, 32, 50, 8.0
+    h, W, y = _rand_case(T, H, V, seed=13)
+    h2 = torch.cat([h, torch.ones((T, 1), dtype=torch.bfloat16)], dim=1)
+    W2 = torch.cat([W, torch.full((V, 1), c, dtype=torch.bfloat16)], dim=1)
+    a = fp64.forward(h, W, y)
+    b = fp64.forward(h2, W2, y)
+    np.testing.assert_allclose(b["logprob"], a["logprob"], atol=1e-12, rtol=0)
+    np.testing.assert_allclose(b["entropy"], a["entropy"], atol=1e-12, rtol=0)
+    np.testing.assert_allclose(b["lse"], a["lse"] + c, atol=1e-12, rtol=0)
+
+
+def test_one_hot_design_exact_logits():
+    V = H = 16
+    a = 3.5
+    W = torch.eye(V, dtype=torch.bfloat16)
+    ks = [0, 5, 15, 7]
+    h = torch.zeros((len(ks), H), dtype=torch.bfloat16)
+    for t, k in enumerate(ks):
+        h[t, k] = a
+    y = torch.tensor([0, 6, 15, 3], dtype=torch.int32)
+    out = fp64.forward(h, W, y)
+    S = math.exp(a) + V - 1
+    for t, k in enumerate(ks):
+        lp = (a if int(y[t]) == k else 0.0) - math.log(S)
+        ent = math.log(S) - a * math.exp(a) / S
+        assert abs(out["logprob"][t] - lp) < 1e-13
+        assert abs(out["entropy"][t] - ent) < 1e-13
+
+
+@pytest.mark.parametrize("delta", [5.0, 12.0, 20.0])
+def test_peaked_row_entropy_closed_form(delta):
+    # one logit at delta, V-1 logits at 0:  eps = (V-1) e^-delta,
+    # H = log1p(eps) + delta * eps / (1 + eps)   (a rearrangement that is exact and stable).
+    V = 16
+    W = torch.eye(V, dtype=torch.bfloat16)
+    h = torch.zeros((1, V), dtype=torch.bfloat16)
+    h[0, 3] = delta
+    out = fp64.forward(h, W, torch.tensor([3], dtype=torch.int32))
+    eps = (V - 1) * math.exp(-delta)
+    ent = math.log1p(eps) + delta * eps / (1 + eps)
+    assert abs(out["entropy"][0] - ent) <= 1e-6 * ent
+    assert abs(out["logprob"][0] + math.log1p(eps)) <= 1e-6 * math.log1p(eps)
+
+
+# --------------------------------------------------------------------------------------------
+# backward
+# --------------------------------------------------------------------------------------------
+
+def _objective(h, W, y, g):
+    """sum_t g_t * logprob_t for in-range labels, and the gradient convention's objective
+    -g_t * lse_t for out-of-range labels (their backward keeps only the -softmax term)."""
+    out = fp64.forward(h, W, y)
+    V = W.shape[0]
+    valid = (y >= 0) & (y < V)
+    return float(np.sum(np.where(valid, g * out["logprob"], -g * out["lse"])))
+
+
+def test_backward_matches_central_differences():
+    T, H, V = 3, 5, 4
+    rng = np.random.default_rng(0)
+    h = rng.normal(size=(T, H))
+    W = rng.normal(size=(V, H)) * 0.7
+    y = np.array([1, -1, 3])
+    g = rng.normal(size=T)
+    gh, gW = fp64.backward(h, W, y, g)
+    eps = 1e-6
+    for arr, grad in ((h, gh), (W, gW)):
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            old = arr[idx]
+            arr[idx] = old + eps
+            fp = _objective(h, W, y, g)
+            arr[idx] = old - eps
+            fm = _objective(h, W, y, g)
+            arr[idx] = old
+            num[idx] = (fp - fm) / (2 * eps)
+        np.testing.assert_allclose(grad, num, rtol=1e-6, atol=1e-8)
+
+
+def test_backward_zero_hidden_closed_form():
+    T, H, V = 4, 6, 9
+    W = synth.weight(V, H, 3, 0.5)
+    h = torch.zeros((T, H), dtype=torch.bfloat16)
+    y = synth.labels(T, V, 3)
+    g = synth.upstream_grad(T, 3)
+    gh, gW = fp64.backward(h, W, y, g)
+    assert np.all(gW == 0.0)
+    Wf = fp64.to_f64(W)
+    expect = fp64.to_f64(g)[:, None] * (Wf[y.long().numpy()] - Wf.mean(axis=0)[None, :])
+    np.testing.assert_allclose(gh, expect, atol=1e-13, rtol=0)
+
+
+def test_grad_weight_column_sums():
+    T, H, V = 7, 12, 10
+    h, W, y = _rand_case(T, H, V, seed=17)
+    y = y.clone()
+    y[3] = V + 4   # out of range
+    g = synth.upstream_grad(T, 17)
+    _, gW = fp64.backward(h, W, y, g)
+    # rows of dz sum to 0 except for out-of-range labels, whose rows sum to -g_t
+    hf, gf = fp64.to_f64(h), fp64.to_f64(g)
+    expect = -gf[3] * hf[3]
+    np.testing.assert_allclose(gW.sum(axis=0), expect, atol=1e-12, rtol=0)
