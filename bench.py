@@ -1,0 +1,157 @@
+"""Benchmark of the fused LM-head log-prob on one MI355X.
+
+Default workload: the forward (log-prob + entropy) at T=8192 tokens, H=4096, V=152064, bf16
+inputs with the peaked-weight recipe (1% of weight rows x10), synthetic and seeded.
+
+A step is one pass of the whole hot path over the batch: lmhead_logprob_fwd, i.e. the logit-tile
+GEMM with its per-chunk records (stage 1) and the fixed-order fold (stage 2), inputs resident in
+HBM.  W warm-up steps, then K timed steps bracketed by torch.cuda.synchronize(); every stage
+launch is also bracketed by HIP events on the stream the library launches on, which gives the
+dominant kernel's average duration for the roofline.
+
+Prints ONE JSON line.  ``--gpus N`` with N > 1 is not supported: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import lm_head_log_lmhead_amd as lmh  # noqa: E402
+import synth  # noqa: E402
+
+METRIC = "fused LM-head logprob tokens/s + % bf16 MFMA peak, T=8192 H=4096 V=152064"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="fwd_T8192_H4096_V152064_peaked", choices=sorted(synth.WORKLOADS))
+    p.add_argument("--cpu-sample-rows", type=int, default=256,
+                   help="rows of the workload the CPU oracle is timed on (0 disables the CPU baseline)")
+    p.add_argument("--copy-bytes", type=int, default=0,
+                   help="also run a plain device copy of this many bytes (counter calibration)")
+    return p.parse_args()
+
+
+def cpu_baseline(x, rows: int, name: str):
+    """Times the fp64 CPU oracle (as it stands) on the first `rows` rows of the same inputs."""
+    from oracle import fp64
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        cores = os.cpu_count()
+    h = x.hidden[:rows]
+    y = x.labels[:rows]
+    W = fp64.to_f64(x.weight)          # conversion is outside the timed region
+    t0 = time.perf_counter()
+    fp64.forward(h, W, y, entropy=True)
+    dt = time.perf_counter() - t0
+    return {"value": rows / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {rows} of {x.hidden.shape[0]} rows of {name} (fp64 numpy, logprob+entropy), "
+                      f"{dt:.1f} s"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); multi-GPU sharding is not part of "
+              "this build", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    wl = synth.WORKLOADS[a.workload]
+    T, H, V = wl.T, wl.H, wl.V
+    dev = torch.device("cuda:0")
+    print(f"[bench] generating {a.workload}", file=sys.stderr, flush=True)
+    x = synth.make_workload(a.workload, seed=0)
+    h, w, y = x.hidden.to(dev), x.weight.to(dev), x.labels.to(dev)
+    lp = torch.empty(T, dtype=torch.float32, device=dev)
+    ent = torch.empty(T, dtype=torch.float32, device=dev) if wl.entropy else None
+    lse = torch.empty(T, dtype=torch.float32, device=dev)
+    ws = torch.empty(lmh.lmhead_logprob_fwd_workspace_size(T, H, V), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    if a.copy_bytes:
+        src = torch.empty(a.copy_bytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record(stream)
+        lmh.lmhead_logprob_fwd_partials(h, w, y, ws, stream)
+        if evs is not None:
+            evs[1].record(stream)
+        lmh.lmhead_logprob_fwd_finalize(y, T, H, V, lp, ent, lse, ws, stream)
+        if evs is not None:
+            evs[2].record(stream)
+
+    print(f"[bench] warmup {a.warmup}", file=sys.stderr, flush=True)
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(a.steps)]
+    print(f"[bench] timing {a.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    k1 = sum(e[0].elapsed_time(e[1]) for e in evs) / a.steps       # ms, stage 1 (logit tiles + records)
+    k2 = sum(e[1].elapsed_time(e[2]) for e in evs) / a.steps       # ms, stage 2 (fold)
+    ms = wall * 1e3 / a.steps
+    flops = 2.0 * T * H * V
+    k1_tflops = flops / (k1 * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": a.workload, "T": T, "H": H, "V": V, "entropy": bool(wl.entropy)},
+        "tflops": flops / (ms * 1e-3) / 1e12,
+        "pct_bf16_mfma_peak": 100.0 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "stage_ms": {"fwd_partials": k1, "fwd_finalize": k2},
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "fwd_partials_kernel",
+            "achieved": k1_tflops,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": k1_tflops / PEAK_BF16_TFLOPS,
+            "traffic": None,
+        },
+        "hbm_gbs_algorithmic": (2.0 * V * H + 2.0 * T * H + 12.0 * T) / (ms * 1e-3) / 1e9,
+    }
+    if a.cpu_sample_rows > 0:
+        print(f"[bench] timing the CPU oracle on {a.cpu_sample_rows} rows", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(x, min(a.cpu_sample_rows, T), a.workload)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

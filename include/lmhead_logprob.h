@@ -1,0 +1,126 @@
+/*
+ * lmhead_logprob.h — C ABI of the fused LM-head log-prob for AMD Instinct MI355X (gfx950).
+ *
+ * What it computes.  For every token row t of hidden[T,H] and the LM-head weight[V,H]:
+ *   z_t      = hidden_t . weight^T                    (fp32 logits over the whole vocabulary,
+ *                                                      accumulated from bf16 products; never
+ *                                                      written to memory)
+ *   lse_t    = log sum_j exp(z_tj)
+ *   logprob_t = z_t,y_t - lse_t, written as (z_y - max) - log(sum exp(z - max)), i.e. the fp32
+ *              log-softmax over the full vocabulary gathered at the label
+ *              (verl PR #8026 "batch-invariant actor forward and sampler log-prob formula",
+ *              first review: the sampler formula, fp32 log_softmax then gather, and the note that
+ *              per-row or chunked evaluation gives the same value as one big log_softmax);
+ *   entropy_t = -sum_j p_tj log p_tj of the same softmax (metric only, no gradient;
+ *              SkyRL PR #1765 "[megatron] Triton backend for fused LM-head log-prob",
+ *              maintainer review and PR summary: entropy stays no-grad).
+ * The [T,V] logits are never materialized: the projection is folded into a vocabulary-tiled
+ * online softmax (SkyRL PR #1765, design commit and PR summary).
+ *
+ * Labels outside [0, V) (for example -100 ignore ids) give logprob 0; their entropy is computed
+ * as usual, and their backward keeps only the -softmax term, dz = -g * p (SkyRL PR #1765,
+ * precision-policy commit on the out-of-vocab gradient).
+ *
+ * Batch invariance.  Each row's outputs are bitwise identical whatever T, the row's position in
+ * the batch, or how the caller splits the rows into calls.  The per-row arithmetic is one fixed
+ * sequence: one MFMA instruction shape and one K order over H, a per-row reduction inside a
+ * fixed 128-column vocabulary chunk, and a fold of the chunk records in an order that depends on
+ * V only.  There are no atomics and no T-dependent split of H or V.  (Megatron-LM PR #5897
+ * "Batch-invariant train/inference logprob parity", commit message: a row's output must not
+ * change with the total row count.)
+ *
+ * Conventions for every entry point:
+ *  - Pointers are DEVICE pointers owned by the caller.  The library never allocates, frees or
+ *    synchronizes, and holds no mutable global state; it is thread-safe.
+ *  - Work is enqueued on `stream` and the call returns; outputs are valid when the stream reaches
+ *    that point.  `stream` may be NULL (the default stream).
+ *  - Arguments are validated on the host before anything is launched.  On failure the status is
+ *    returned and nothing is launched.  T == 0 returns LMH_OK and launches nothing.
+ *  - Layouts: hidden bf16 [T,H] row-major contiguous; weight bf16 [V,H] row-major contiguous;
+ *    labels int32 [T]; all per-row outputs fp32 [T]; gradients fp32 row-major contiguous.
+ *  - Requirements: H % 8 == 0, 8 <= H <= 1048576, 1 <= V < 2^31, 0 <= T < 2^31; hidden and
+ *    weight 16-byte aligned; labels, per-row arrays and gradients 4-byte aligned; workspace
+ *    256-byte aligned.  Non-finite inputs give undefined outputs (no error).
+ *  - No C++ exception crosses the ABI.  There is no silent fallback: an unsupported request is
+ *    an error code.
+ */
+#ifndef LMHEAD_LOGPROB_H
+#define LMHEAD_LOGPROB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#if defined(_WIN32)
+#define LMH_API
+#else
+#define LMH_API __attribute__((visibility("default")))
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LMH_OK = 0,
+  LMH_ERR_INVALID_ARG = 1,          /* null required pointer, negative or zero size           */
+  LMH_ERR_UNSUPPORTED = 2,          /* H % 8 != 0, size limits, misaligned pointer              */
+  LMH_ERR_WORKSPACE_TOO_SMALL = 3,  /* workspace_bytes below the *_workspace_size() value       */
+  LMH_ERR_HIP = 4                   /* a kernel launch failed (hipGetLastError after launching) */
+} lmh_status_t;
+
+/* Bytes of workspace lmhead_logprob_fwd needs (also the stage entry points below).  Returns 0 for
+ * invalid sizes.  The workspace holds one 16-byte record per (row, 128-column vocabulary chunk)
+ * plus one float per row. */
+LMH_API size_t lmhead_logprob_fwd_workspace_size(int64_t T, int64_t H, int64_t V);
+
+/* Forward.  logprob is required; entropy and lse may be NULL (not computed / not written).
+ * lse is what lmhead_logprob_bwd needs later. */
+LMH_API lmh_status_t lmhead_logprob_fwd(const void* hidden, const void* weight, const int32_t* labels,
+                                        int64_t T, int64_t H, int64_t V,
+                                        float* logprob, float* entropy, float* lse,
+                                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* The forward as its two stages (lmhead_logprob_fwd is exactly these two calls in order):
+ *  1. _partials runs the vocabulary-tiled logit GEMM and writes, into the workspace, one record
+ *     per (row, vocabulary chunk): (chunk max, count of logits equal to it, sum of exp(z - max)
+ *     over logits below it, sum of exp(z - max)(z - max)) plus the label's logit.
+ *  2. _finalize folds each row's records in a fixed order and writes the outputs.
+ * The workspace contents between the stages are private to the library. */
+LMH_API lmh_status_t lmhead_logprob_fwd_partials(const void* hidden, const void* weight, const int32_t* labels,
+                                                 int64_t T, int64_t H, int64_t V,
+                                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+LMH_API lmh_status_t lmhead_logprob_fwd_finalize(const int32_t* labels, int64_t T, int64_t H, int64_t V,
+                                                 float* logprob, float* entropy, float* lse,
+                                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace lmhead_logprob_bwd needs.  Returns 0 for invalid sizes. */
+LMH_API size_t lmhead_logprob_bwd_workspace_size(int64_t T, int64_t H, int64_t V);
+
+/* Backward of sum_t grad_logprob_t * logprob_t (entropy has no gradient).
+ * dz_tj = g_t * ([j == y_t] - exp(z_tj - lse_t)), the logits being recomputed (SkyRL PR #1765:
+ * design commit, recompute the per-chunk logits in backward; streaming-backward commit, the
+ * -p*g term plus the label term).  dz is rounded to bf16 before the two gradient GEMMs.
+ *   grad_hidden [T,H] fp32 = dz . weight   (written, or NULL to skip)
+ *   grad_weight [V,H] fp32 = dz^T . hidden (overwritten if accumulate_grad_weight == 0, else
+ *                                            added to; NULL to skip)
+ * lse must be the lse[T] written by lmhead_logprob_fwd for the same inputs.  The backward also
+ * needs T < 2^22 (LMH_ERR_UNSUPPORTED otherwise).  T == 0 leaves the gradient buffers untouched.
+ * grad_hidden is bitwise invariant to how rows are split across calls.  grad_weight is
+ * deterministic; splitting the rows at multiples of 64 and accumulating the parts in order with
+ * accumulate_grad_weight = 1 reproduces one call bit for bit. */
+LMH_API lmh_status_t lmhead_logprob_bwd(const void* hidden, const void* weight, const int32_t* labels,
+                                        int64_t T, int64_t H, int64_t V,
+                                        const float* grad_logprob, const float* lse,
+                                        float* grad_hidden, float* grad_weight, int accumulate_grad_weight,
+                                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Static English text for a status code (never NULL). */
+LMH_API const char* lmhead_status_string(lmh_status_t s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LMHEAD_LOGPROB_H */

@@ -1,0 +1,233 @@
+"""Python binding of the fused LM-head log-prob HIP library (MI355X / gfx950).
+
+Thin ctypes layer over ``include/lmhead_logprob.h``: functions with the same names as the C entry
+points, which only marshal torch tensors to device pointers and raise on a non-OK status, plus a
+``torch.autograd.Function`` wrapper.  Every step of the computation runs in the HIP kernels;
+there is no fallback: if the library is not built, importing works but any call raises.
+
+PyTorch provides device memory and the current stream, nothing else.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_lib", "liblmhead_logprob.so")
+
+LMH_OK = 0
+LMH_ERR_INVALID_ARG = 1
+LMH_ERR_UNSUPPORTED = 2
+LMH_ERR_WORKSPACE_TOO_SMALL = 3
+LMH_ERR_HIP = 4
+
+# Entry points declared in include/lmhead_logprob.h, with their ctypes signatures.
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+_SIGNATURES = {
+    "lmhead_logprob_fwd_workspace_size": (_SZ, [_I64, _I64, _I64]),
+    "lmhead_logprob_fwd": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P]),
+    "lmhead_logprob_fwd_partials": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P]),
+    "lmhead_logprob_fwd_finalize": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P]),
+    "lmhead_logprob_bwd_workspace_size": (_SZ, [_I64, _I64, _I64]),
+    "lmhead_logprob_bwd": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, ctypes.c_int, _P, _SZ, _P]),
+    "lmhead_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+}
+
+_lib = None
+
+
+class LmheadError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({lmhead_status_string(status)})")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"HIP library not built: {LIB_PATH} is missing "
+                               "(run `python -c 'import __graft_entry__ as g; g.build()'` at the repo root)")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(l, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = l
+    return _lib
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int, where: str) -> None:
+    if status != LMH_OK:
+        raise LmheadError(status, where)
+
+
+def _check_tensor(t: Optional[torch.Tensor], name: str, dtype, numel: Optional[int] = None) -> None:
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} must have {numel} elements, got {t.numel()}")
+
+
+# ---------------------------------------------------------------------------------------------
+# the C entry points, same names
+# ---------------------------------------------------------------------------------------------
+
+def lmhead_status_string(status: int) -> str:
+    return lib().lmhead_status_string(int(status)).decode()
+
+
+def lmhead_logprob_fwd_workspace_size(T: int, H: int, V: int) -> int:
+    return int(lib().lmhead_logprob_fwd_workspace_size(T, H, V))
+
+
+def lmhead_logprob_bwd_workspace_size(T: int, H: int, V: int) -> int:
+    return int(lib().lmhead_logprob_bwd_workspace_size(T, H, V))
+
+
+def _dims(hidden: torch.Tensor, weight: torch.Tensor):
+    if hidden.dim() != 2 or weight.dim() != 2 or hidden.shape[1] != weight.shape[1]:
+        raise ValueError(f"hidden [T,H] and weight [V,H] expected, got {tuple(hidden.shape)} and {tuple(weight.shape)}")
+    return hidden.shape[0], hidden.shape[1], weight.shape[0]
+
+
+def lmhead_logprob_fwd(hidden, weight, labels, logprob, entropy=None, lse=None, workspace=None, stream=None) -> None:
+    T, H, V = _dims(hidden, weight)
+    _check_tensor(hidden, "hidden", torch.bfloat16)
+    _check_tensor(weight, "weight", torch.bfloat16)
+    _check_tensor(labels, "labels", torch.int32, T)
+    for t, n in ((logprob, "logprob"), (entropy, "entropy"), (lse, "lse")):
+        _check_tensor(t, n, torch.float32, T)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().lmhead_logprob_fwd(_ptr(hidden), _ptr(weight), _ptr(labels), T, H, V, _ptr(logprob), _ptr(entropy),
+                                    _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)), "lmhead_logprob_fwd")
+
+
+def lmhead_logprob_fwd_partials(hidden, weight, labels, workspace, stream=None) -> None:
+    T, H, V = _dims(hidden, weight)
+    _check_tensor(hidden, "hidden", torch.bfloat16)
+    _check_tensor(weight, "weight", torch.bfloat16)
+    _check_tensor(labels, "labels", torch.int32, T)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().lmhead_logprob_fwd_partials(_ptr(hidden), _ptr(weight), _ptr(labels), T, H, V, _ptr(workspace),
+                                             ws_bytes, _stream(stream)), "lmhead_logprob_fwd_partials")
+
+
+def lmhead_logprob_fwd_finalize(labels, T, H, V, logprob, entropy=None, lse=None, workspace=None, stream=None) -> None:
+    _check_tensor(labels, "labels", torch.int32, T)
+    for t, n in ((logprob, "logprob"), (entropy, "entropy"), (lse, "lse")):
+        _check_tensor(t, n, torch.float32, T)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().lmhead_logprob_fwd_finalize(_ptr(labels), T, H, V, _ptr(logprob), _ptr(entropy), _ptr(lse),
+                                             _ptr(workspace), ws_bytes, _stream(stream)), "lmhead_logprob_fwd_finalize")
+
+
+def lmhead_logprob_bwd(hidden, weight, labels, grad_logprob, lse, grad_hidden=None, grad_weight=None,
+                       accumulate_grad_weight: bool = False, workspace=None, stream=None) -> None:
+    T, H, V = _dims(hidden, weight)
+    _check_tensor(hidden, "hidden", torch.bfloat16)
+    _check_tensor(weight, "weight", torch.bfloat16)
+    _check_tensor(labels, "labels", torch.int32, T)
+    _check_tensor(grad_logprob, "grad_logprob", torch.float32, T)
+    _check_tensor(lse, "lse", torch.float32, T)
+    _check_tensor(grad_hidden, "grad_hidden", torch.float32, T * H)
+    _check_tensor(grad_weight, "grad_weight", torch.float32, V * H)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().lmhead_logprob_bwd(_ptr(hidden), _ptr(weight), _ptr(labels), T, H, V, _ptr(grad_logprob), _ptr(lse),
+                                    _ptr(grad_hidden), _ptr(grad_weight), int(bool(accumulate_grad_weight)),
+                                    _ptr(workspace), ws_bytes, _stream(stream)), "lmhead_logprob_bwd")
+
+
+# ---------------------------------------------------------------------------------------------
+# allocation helpers and the autograd wrapper
+# ---------------------------------------------------------------------------------------------
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    # torch's caching allocator returns 256-byte (or better) aligned blocks
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def forward(hidden: torch.Tensor, weight: torch.Tensor, labels: torch.Tensor, entropy: bool = False,
+            want_lse: bool = False, stream=None):
+    """Allocate outputs and workspace with torch and run lmhead_logprob_fwd.
+
+    Returns (logprob [T] fp32, entropy [T] fp32 or None, lse [T] fp32 or None)."""
+    T, H, V = _dims(hidden, weight)
+    dev = hidden.device
+    lp = torch.empty(T, dtype=torch.float32, device=dev)
+    ent = torch.empty(T, dtype=torch.float32, device=dev) if entropy else None
+    lse = torch.empty(T, dtype=torch.float32, device=dev) if want_lse else None
+    ws = _workspace(lmhead_logprob_fwd_workspace_size(T, H, V), dev)
+    lmhead_logprob_fwd(hidden, weight, labels, lp, ent, lse, ws, stream)
+    return lp, ent, lse
+
+
+def backward(hidden, weight, labels, grad_logprob, lse, need_hidden=True, need_weight=True, stream=None):
+    """Allocate gradients and workspace with torch and run lmhead_logprob_bwd (overwrite mode)."""
+    T, H, V = _dims(hidden, weight)
+    dev = hidden.device
+    gh = torch.empty((T, H), dtype=torch.float32, device=dev) if need_hidden else None
+    gw = torch.empty((V, H), dtype=torch.float32, device=dev) if need_weight else None
+    ws = _workspace(lmhead_logprob_bwd_workspace_size(T, H, V), dev)
+    lmhead_logprob_bwd(hidden, weight, labels, grad_logprob, lse, gh, gw, False, ws, stream)
+    return gh, gw
+
+
+class _FusedLogprob(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, hidden, weight, labels, want_entropy):
+        lp, ent, lse = forward(hidden, weight, labels, entropy=want_entropy, want_lse=True)
+        ctx.save_for_backward(hidden, weight, labels, lse)
+        if ent is not None:
+            ctx.mark_non_differentiable(ent)
+        return lp, ent
+
+    @staticmethod
+    def backward(ctx, grad_lp, grad_ent):
+        hidden, weight, labels, lse = ctx.saved_tensors
+        if grad_ent is not None and bool(torch.any(grad_ent != 0)):
+            raise RuntimeError("entropy has no gradient in the fused LM-head log-prob")
+        g = grad_lp.contiguous().to(torch.float32)
+        gh, gw = backward(hidden, weight, labels, g, lse, ctx.needs_input_grad[0], ctx.needs_input_grad[1])
+        return gh, gw, None, None
+
+
+def logprob(hidden: torch.Tensor, weight: torch.Tensor, labels: torch.Tensor, entropy: bool = False):
+    """Fused LM-head log-prob with autograd.
+
+    hidden [..., H] (any float dtype; cast to weight's dtype before the projection, and the
+    gradient cast back, as the pages' adapter does), weight [V, H] bf16, labels [...] integer.
+    Leading dimensions are flattened to token rows.  Returns (logprob [...], entropy [...] or
+    None), fp32; entropy carries no gradient."""
+    if weight.dtype != torch.bfloat16:
+        raise ValueError("weight must be bf16")
+    lead = hidden.shape[:-1]
+    h2 = hidden.reshape(-1, hidden.shape[-1])
+    h2 = h2.to(weight.dtype).contiguous()   # differentiable: grad_hidden is cast back by autograd
+    y = labels.reshape(-1).to(torch.int32).contiguous()
+    lp, ent = _FusedLogprob.apply(h2, weight.contiguous(), y, entropy)
+    return lp.reshape(lead), (ent.reshape(lead) if ent is not None else None)

@@ -1,0 +1,193 @@
+// api.hip — the C ABI (include/lmhead_logprob.h): host-side validation, workspace carving and
+// launch.  Every check runs before the first launch; a failed check launches nothing.
+#include "lmhead_logprob.h"
+
+#include "kernels.hpp"
+
+namespace {
+
+using lmh::FwdArgs;
+
+constexpr int64_t MAX_H = 1 << 20;
+constexpr int64_t MAX_V = INT32_MAX;  // exclusive bound 2^31 - 1 rows
+constexpr int64_t MAX_T = INT32_MAX;
+// backward: token-major transposed operands are read through 32-bit buffer offsets (256 rows x T)
+constexpr int64_t MAX_T_BWD = int64_t(1) << 22;
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Sizes: returns LMH_OK, or the error for the first violated rule.
+lmh_status_t check_sizes(int64_t T, int64_t H, int64_t V) {
+  if (T < 0 || H <= 0 || V <= 0) return LMH_ERR_INVALID_ARG;
+  if (H % 8 != 0 || H > MAX_H || V >= MAX_V || T >= MAX_T) return LMH_ERR_UNSUPPORTED;
+  // every size derived below (records, workspace offsets) must fit in 64 bits comfortably
+  const int64_t n_c = (V + lmh::VOCAB_CHUNK - 1) / lmh::VOCAB_CHUNK;
+  if (T > 0 && n_c > (int64_t(1) << 40) / T) return LMH_ERR_UNSUPPORTED;
+  return LMH_OK;
+}
+
+struct FwdWs {
+  size_t rec_off, zy_off, total;
+};
+
+FwdWs fwd_ws(int64_t T, int64_t V) {
+  const int64_t n_c = (V + lmh::VOCAB_CHUNK - 1) / lmh::VOCAB_CHUNK;
+  FwdWs w;
+  w.rec_off = 0;
+  w.zy_off = align256((size_t)n_c * (size_t)T * 16);
+  w.total = w.zy_off + align256((size_t)T * 4);
+  return w;
+}
+
+lmh_status_t check_inputs(const void* hidden, const void* weight, const int32_t* labels) {
+  if (!hidden || !weight || !labels) return LMH_ERR_INVALID_ARG;
+  if (!aligned(hidden, 16) || !aligned(weight, 16) || !aligned(labels, 4)) return LMH_ERR_UNSUPPORTED;
+  return LMH_OK;
+}
+
+lmh_status_t check_ws(const void* ws, size_t bytes, size_t need) {
+  if (bytes < need) return LMH_ERR_WORKSPACE_TOO_SMALL;
+  if (need > 0 && !ws) return LMH_ERR_INVALID_ARG;
+  if (ws && !aligned(ws, 256)) return LMH_ERR_UNSUPPORTED;
+  return LMH_OK;
+}
+
+lmh_status_t check_out(const float* p, bool required) {
+  if (!p) return required ? LMH_ERR_INVALID_ARG : LMH_OK;
+  return aligned(p, 4) ? LMH_OK : LMH_ERR_UNSUPPORTED;
+}
+
+lmh_status_t launched() { return hipGetLastError() == hipSuccess ? LMH_OK : LMH_ERR_HIP; }
+
+FwdArgs make_fwd_args(const void* hidden, const void* weight, const int32_t* labels, int64_t T, int64_t H,
+                      int64_t V, float* logprob, float* entropy, float* lse, void* workspace) {
+  const FwdWs w = fwd_ws(T, V);
+  char* ws = static_cast<char*>(workspace);
+  FwdArgs a;
+  a.hidden = static_cast<const __bf16*>(hidden);
+  a.weight = static_cast<const __bf16*>(weight);
+  a.labels = labels;
+  a.T = (int)T;
+  a.H = (int)H;
+  a.V = (int)V;
+  a.rec = reinterpret_cast<lmh::f32x4*>(ws + w.rec_off);
+  a.zy = reinterpret_cast<float*>(ws + w.zy_off);
+  a.logprob = logprob;
+  a.entropy = entropy;
+  a.lse = lse;
+  return a;
+}
+
+#define LMH_TRY(expr)                      \
+  do {                                     \
+    const lmh_status_t s_ = (expr);        \
+    if (s_ != LMH_OK) return s_;           \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+size_t lmhead_logprob_fwd_workspace_size(int64_t T, int64_t H, int64_t V) {
+  if (check_sizes(T, H, V) != LMH_OK) return 0;
+  return fwd_ws(T, V).total;
+}
+
+lmh_status_t lmhead_logprob_fwd_partials(const void* hidden, const void* weight, const int32_t* labels, int64_t T,
+                                         int64_t H, int64_t V, void* workspace, size_t workspace_bytes,
+                                         hipStream_t stream) {
+  LMH_TRY(check_sizes(T, H, V));
+  if (T == 0) return LMH_OK;
+  LMH_TRY(check_inputs(hidden, weight, labels));
+  LMH_TRY(check_ws(workspace, workspace_bytes, fwd_ws(T, V).total));
+  (void)hipGetLastError();  // clear any stale error so the check after launching sees only ours
+  lmh::launch_fwd_partials(make_fwd_args(hidden, weight, labels, T, H, V, nullptr, nullptr, nullptr, workspace),
+                           stream);
+  return launched();
+}
+
+lmh_status_t lmhead_logprob_fwd_finalize(const int32_t* labels, int64_t T, int64_t H, int64_t V, float* logprob,
+                                         float* entropy, float* lse, void* workspace, size_t workspace_bytes,
+                                         hipStream_t stream) {
+  LMH_TRY(check_sizes(T, H, V));
+  if (T == 0) return LMH_OK;
+  if (!labels) return LMH_ERR_INVALID_ARG;
+  if (!aligned(labels, 4)) return LMH_ERR_UNSUPPORTED;
+  LMH_TRY(check_out(logprob, true));
+  LMH_TRY(check_out(entropy, false));
+  LMH_TRY(check_out(lse, false));
+  LMH_TRY(check_ws(workspace, workspace_bytes, fwd_ws(T, V).total));
+  (void)hipGetLastError();
+  lmh::launch_fwd_finalize(make_fwd_args(nullptr, nullptr, labels, T, H, V, logprob, entropy, lse, workspace),
+                           stream);
+  return launched();
+}
+
+lmh_status_t lmhead_logprob_fwd(const void* hidden, const void* weight, const int32_t* labels, int64_t T, int64_t H,
+                                int64_t V, float* logprob, float* entropy, float* lse, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  LMH_TRY(check_sizes(T, H, V));
+  if (T == 0) return LMH_OK;
+  LMH_TRY(check_inputs(hidden, weight, labels));
+  LMH_TRY(check_out(logprob, true));
+  LMH_TRY(check_out(entropy, false));
+  LMH_TRY(check_out(lse, false));
+  LMH_TRY(check_ws(workspace, workspace_bytes, fwd_ws(T, V).total));
+  (void)hipGetLastError();
+  const FwdArgs a = make_fwd_args(hidden, weight, labels, T, H, V, logprob, entropy, lse, workspace);
+  lmh::launch_fwd_partials(a, stream);
+  if (hipGetLastError() != hipSuccess) return LMH_ERR_HIP;
+  lmh::launch_fwd_finalize(a, stream);
+  return launched();
+}
+
+size_t lmhead_logprob_bwd_workspace_size(int64_t T, int64_t H, int64_t V) {
+  if (check_sizes(T, H, V) != LMH_OK) return 0;
+  return lmh::bwd_layout(T, H, V).total;
+}
+
+lmh_status_t lmhead_logprob_bwd(const void* hidden, const void* weight, const int32_t* labels, int64_t T, int64_t H,
+                                int64_t V, const float* grad_logprob, const float* lse, float* grad_hidden,
+                                float* grad_weight, int accumulate_grad_weight, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  LMH_TRY(check_sizes(T, H, V));
+  if (accumulate_grad_weight != 0 && accumulate_grad_weight != 1) return LMH_ERR_INVALID_ARG;
+  if (T >= MAX_T_BWD) return LMH_ERR_UNSUPPORTED;
+  if (T == 0) return LMH_OK;  // no rows: nothing is launched and the gradient buffers are untouched
+  LMH_TRY(check_inputs(hidden, weight, labels));
+  if (!grad_logprob || !lse) return LMH_ERR_INVALID_ARG;
+  if (!aligned(grad_logprob, 4) || !aligned(lse, 4)) return LMH_ERR_UNSUPPORTED;
+  LMH_TRY(check_out(grad_hidden, false));
+  LMH_TRY(check_out(grad_weight, false));
+  const lmh::BwdLayout L = lmh::bwd_layout(T, H, V);
+  LMH_TRY(check_ws(workspace, workspace_bytes, L.total));
+  if (!grad_hidden && !grad_weight) return LMH_OK;
+  (void)hipGetLastError();
+  lmh::BwdArgs a;
+  a.hidden = static_cast<const __bf16*>(hidden);
+  a.weight = static_cast<const __bf16*>(weight);
+  a.labels = labels;
+  a.grad = grad_logprob;
+  a.lse = lse;
+  a.grad_hidden = grad_hidden;
+  a.grad_weight = grad_weight;
+  a.accumulate_gw = accumulate_grad_weight;
+  a.ws = static_cast<char*>(workspace);
+  a.L = L;
+  lmh::launch_bwd(a, stream);
+  return launched();
+}
+
+const char* lmhead_status_string(lmh_status_t s) {
+  switch (s) {
+    case LMH_OK: return "ok";
+    case LMH_ERR_INVALID_ARG: return "invalid argument (null required pointer or non-positive size)";
+    case LMH_ERR_UNSUPPORTED: return "unsupported (H % 8 != 0, a size limit, or a misaligned pointer)";
+    case LMH_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case LMH_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

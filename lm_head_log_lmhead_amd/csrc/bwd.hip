@@ -1,0 +1,260 @@
+// bwd.hip — backward kernels of the fused LM-head log-prob.
+//
+// The backward of sum_t g_t * logprob_t recomputes the logits instead of keeping them (SkyRL PR
+// #1765 "[megatron] Triton backend for fused LM-head log-prob", design commit: per-chunk logits
+// are recomputed in backward) and uses dz_tj = g_t * ([j == y_t] - p_tj) with p = exp(z - lse);
+// a label outside [0, V) contributes no label term, so dz = -g * p there (same PR,
+// precision-policy commit; streaming-backward commit: exp of the log-softmax, negated, times the
+// upstream gradient, plus the upstream gradient at the label).
+//
+// The vocabulary is walked in fixed steps of Vs rows.  Per step:
+//   K3 bwd_dz     : logit tile recompute (same MFMA main loop and tiles as the forward) and
+//                   dz rounded to bf16, written token-major into a [T x Vs] workspace slab;
+//   transposes    : dz -> dz^T [Vs x Tp] and W_step -> W_step^T [H x Vs] (token- / vocab-
+//                   contiguous copies, so both gradient GEMMs read K-contiguous operands);
+//   K5 grad_weight: grad_W[step rows] (+)= dz^T . h  (K = tokens, one chain per element, no split)
+//   K4 grad_hidden: grad_h += dz . W_step           (K = vocabulary; the accumulator is loaded
+//                   from grad_h so the chain simply continues across steps)
+// No atomics anywhere; every output element is produced by exactly one lane.
+#include "kernels.hpp"
+
+namespace lmh {
+
+// ---------------------------------------------------------------------------------------------
+// K3: dz tiles
+// ---------------------------------------------------------------------------------------------
+
+constexpr int DZ_PITCH = WAVE_M * 2 + 16;  // bytes per staged token row (padded against conflicts)
+
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::NTHREADS) void bwd_dz_kernel(
+    const __bf16* __restrict__ hidden, const __bf16* __restrict__ weight, const int* __restrict__ labels,
+    const float* __restrict__ grad, const float* __restrict__ lse, int T, int H, int V, int vs0, int Vc,
+    int Vs, int n_mt, int n_nt, __bf16* __restrict__ dz) {
+  constexpr int STAGE_OUT = Cfg::NWAVES * Cfg::WAVE_N * DZ_PITCH;
+  constexpr int LDS = Cfg::LDS_BYTES > STAGE_OUT ? Cfg::LDS_BYTES : STAGE_OUT;
+  __shared__ __attribute__((aligned(16))) char lds[LDS];
+  int mt, nt;
+  tile_coords<8>(blockIdx.x, gridDim.x, n_mt, n_nt, mt, nt);
+  const int v0 = mt * Cfg::TM;  // local vocabulary row inside the step
+  const int t0 = nt * Cfg::TN;
+  f32x16 acc[MSUB][Cfg::NSUB];
+#pragma unroll
+  for (int m = 0; m < MSUB; ++m)
+#pragma unroll
+    for (int n = 0; n < Cfg::NSUB; ++n) acc[m][n] = (f32x16)(0.0f);
+  tile_mainloop<Cfg>(weight + (int64_t)(vs0 + v0) * H, H, min(Cfg::TM, Vc - v0), hidden + (int64_t)t0 * H, H,
+                     min(Cfg::TN, T - t0), H, lds, acc);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave % Cfg::WM, wn = wave / Cfg::WM;
+  const int j = lane & 31;
+  const int hf = lane >> 5;
+  const int wv = v0 + wm * WAVE_M;             // local column of this wavefront's first entry
+  const int tok0 = t0 + wn * Cfg::WAVE_N;
+  char* wl = lds + wave * Cfg::WAVE_N * DZ_PITCH;
+
+#pragma unroll
+  for (int n = 0; n < Cfg::NSUB; ++n) {
+    const int tok = tok0 + n * 32 + j;
+    const bool tok_ok = tok < T;
+    const float g = tok_ok ? grad[tok] : 0.f;
+    const float L = tok_ok ? lse[tok] : 0.f;
+    const int y = tok_ok ? labels[tok] : -1;
+#pragma unroll
+    for (int m = 0; m < MSUB; ++m)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        bf16x4 pk;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = m * 32 + 8 * g4 + 4 * hf + q;
+          const int v = vs0 + wv + col;
+          const float p = __builtin_amdgcn_exp2f((acc[m][n][4 * g4 + q] - L) * LOG2E);
+          const float oh = v == y ? 1.f : 0.f;
+          const float d = v < V ? g * (oh - p) : 0.f;
+          pk[q] = (__bf16)d;
+        }
+        *reinterpret_cast<bf16x4*>(wl + (n * 32 + j) * DZ_PITCH + (m * 32 + 8 * g4 + 4 * hf) * 2) = pk;
+      }
+  }
+  __syncthreads();
+  // copy the wavefront's [WAVE_N tokens x 128 entries] block out, 16 bytes per lane
+  constexpr int CHUNKS = Cfg::WAVE_N * (WAVE_M / 8);
+#pragma unroll
+  for (int i = 0; i < CHUNKS / 64; ++i) {
+    const int q = lane + 64 * i;
+    const int row = q / (WAVE_M / 8);
+    const int c = q % (WAVE_M / 8);
+    const int tok = tok0 + row;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(wl + row * DZ_PITCH + c * 16);
+    if (tok < T) *reinterpret_cast<u32x4*>(dz + (int64_t)tok * Vs + wv + c * 8) = v;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// transposes: dst[c][r] = src[r][c] for r < R, 0 for R <= r < Rp; c < C (C % 8 == 0)
+// ---------------------------------------------------------------------------------------------
+
+constexpr int TR_TILE = 64;
+
+__global__ __launch_bounds__(256) void transpose_pad_kernel(const __bf16* __restrict__ src, int64_t lds_, int R,
+                                                            int C, __bf16* __restrict__ dst, int64_t ldd, int Rp) {
+  __shared__ unsigned short tile[TR_TILE][TR_TILE + 2];
+  const int r0 = blockIdx.x * TR_TILE;
+  const int c0 = blockIdx.y * TR_TILE;
+  const int tid = threadIdx.x;
+  const unsigned short* s16 = reinterpret_cast<const unsigned short*>(src);
+  // load: 64 rows x 8 chunks of 8 elements, 2 chunks per thread
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int q = tid + 256 * i;
+    const int rr = q >> 3, cc = (q & 7) * 8;
+    const int r = r0 + rr, c = c0 + cc;
+    u32x4 v = (u32x4)(0u);
+    if (r < R && c < C) v = *reinterpret_cast<const u32x4*>(s16 + (int64_t)r * lds_ + c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      tile[rr][cc + 2 * e] = (unsigned short)(v[e] & 0xffffu);
+      tile[rr][cc + 2 * e + 1] = (unsigned short)(v[e] >> 16);
+    }
+  }
+  __syncthreads();
+  unsigned short* d16 = reinterpret_cast<unsigned short*>(dst);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int q = tid + 256 * i;
+    const int cc = q >> 3, rr = (q & 7) * 8;
+    const int c = c0 + cc, r = r0 + rr;
+    if (c >= C || r >= Rp) continue;
+    u32x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      v[e] = (unsigned)tile[rr + 2 * e][cc] | ((unsigned)tile[rr + 2 * e + 1][cc] << 16);
+    *reinterpret_cast<u32x4*>(d16 + (int64_t)c * ldd + r) = v;
+  }
+}
+
+static void launch_transpose(const __bf16* src, int64_t ld_src, int R, int C, __bf16* dst, int64_t ld_dst, int Rp,
+                             hipStream_t stream) {
+  dim3 grid((Rp + TR_TILE - 1) / TR_TILE, (C + TR_TILE - 1) / TR_TILE);
+  hipLaunchKernelGGL(transpose_pad_kernel, grid, dim3(256), 0, stream, src, ld_src, R, C, dst, ld_dst, Rp);
+}
+
+// ---------------------------------------------------------------------------------------------
+// K4 / K5: C[M x N] fp32 = (accumulate ? C : 0) + A[M x K] . B[N x K]^T
+// ---------------------------------------------------------------------------------------------
+
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::NTHREADS) void gemm_tn_f32_kernel(
+    const __bf16* __restrict__ A, int64_t lda, int M, const __bf16* __restrict__ B, int64_t ldb, int N, int K,
+    float* __restrict__ C, int64_t ldc, int accumulate, int n_mt, int n_nt) {
+  __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
+  int mt, nt;
+  tile_coords<8>(blockIdx.x, gridDim.x, n_mt, n_nt, mt, nt);
+  const int m0 = mt * Cfg::TM;
+  const int n0 = nt * Cfg::TN;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave % Cfg::WM, wn = wave / Cfg::WM;
+  const int rbase = m0 + wm * WAVE_M;
+  const int cbase = n0 + wn * Cfg::WAVE_N + (lane & 31);
+
+  f32x16 acc[MSUB][Cfg::NSUB];
+#pragma unroll
+  for (int m = 0; m < MSUB; ++m)
+#pragma unroll
+    for (int n = 0; n < Cfg::NSUB; ++n)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = rbase + m * 32 + acc_row(r, lane);
+        const int col = cbase + n * 32;
+        acc[m][n][r] = (accumulate && row < M && col < N) ? C[(int64_t)row * ldc + col] : 0.f;
+      }
+
+  tile_mainloop<Cfg>(A + (int64_t)m0 * lda, lda, min(Cfg::TM, M - m0), B + (int64_t)n0 * ldb, ldb,
+                     min(Cfg::TN, N - n0), K, lds, acc);
+
+#pragma unroll
+  for (int m = 0; m < MSUB; ++m)
+#pragma unroll
+    for (int n = 0; n < Cfg::NSUB; ++n)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = rbase + m * 32 + acc_row(r, lane);
+        const int col = cbase + n * 32;
+        if (row < M && col < N) C[(int64_t)row * ldc + col] = acc[m][n][r];
+      }
+}
+
+template <class Cfg>
+static void launch_gemm_tn(const __bf16* A, int64_t lda, int M, const __bf16* B, int64_t ldb, int N, int K, float* C,
+                           int64_t ldc, int accumulate, hipStream_t stream) {
+  const int n_mt = (M + Cfg::TM - 1) / Cfg::TM;
+  const int n_nt = (N + Cfg::TN - 1) / Cfg::TN;
+  hipLaunchKernelGGL(gemm_tn_f32_kernel<Cfg>, dim3(n_mt * n_nt), dim3(Cfg::NTHREADS), 0, stream, A, lda, M, B, ldb,
+                     N, K, C, ldc, accumulate, n_mt, n_nt);
+}
+
+// ---------------------------------------------------------------------------------------------
+// orchestration
+// ---------------------------------------------------------------------------------------------
+
+static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+BwdLayout bwd_layout(int64_t T, int64_t H, int64_t V) {
+  BwdLayout L{};
+  L.T = (int)T;
+  L.H = (int)H;
+  L.V = (int)V;
+  L.Tp = (int)((T + 63) / 64 * 64);
+  const int64_t vr = (V + 255) / 256 * 256;
+  L.Vs = (int)(vr < BWD_VOCAB_STEP ? vr : BWD_VOCAB_STEP);
+  size_t off = 0;
+  L.off_dz = off;
+  off += align256((size_t)T * L.Vs * 2);
+  L.off_dzt = off;
+  off += align256((size_t)L.Vs * L.Tp * 2);
+  L.off_wt = off;
+  off += align256((size_t)H * L.Vs * 2);
+  L.off_ht = off;
+  off += align256((size_t)H * L.Tp * 2);
+  L.total = off;
+  return L;
+}
+
+using CfgDz = TileCfg<2, 2, 4>;
+using CfgGrad = TileCfg<2, 2, 4>;
+
+void launch_bwd(const BwdArgs& a, hipStream_t stream) {
+  const BwdLayout& L = a.L;
+  __bf16* dz = reinterpret_cast<__bf16*>(a.ws + L.off_dz);
+  __bf16* dzt = reinterpret_cast<__bf16*>(a.ws + L.off_dzt);
+  __bf16* wt = reinterpret_cast<__bf16*>(a.ws + L.off_wt);
+  __bf16* ht = reinterpret_cast<__bf16*>(a.ws + L.off_ht);
+  if (!a.grad_hidden && !a.grad_weight) return;
+  if (a.grad_weight) launch_transpose(a.hidden, L.H, L.T, L.H, ht, L.Tp, L.Tp, stream);
+
+  for (int vs0 = 0; vs0 < L.V; vs0 += L.Vs) {
+    const int Vc = L.V - vs0 < L.Vs ? L.V - vs0 : L.Vs;
+    {
+      const int n_mt = (Vc + CfgDz::TM - 1) / CfgDz::TM;
+      const int n_nt = (L.T + CfgDz::TN - 1) / CfgDz::TN;
+      hipLaunchKernelGGL(bwd_dz_kernel<CfgDz>, dim3(n_mt * n_nt), dim3(CfgDz::NTHREADS), 0, stream, a.hidden,
+                         a.weight, a.labels, a.grad, a.lse, L.T, L.H, L.V, vs0, Vc, L.Vs, n_mt, n_nt, dz);
+    }
+    const int Vc8 = (Vc + 7) / 8 * 8;  // dz columns past Vc inside the written tiles are zeros
+    if (a.grad_weight) {
+      launch_transpose(dz, L.Vs, L.T, Vc8, dzt, L.Tp, L.Tp, stream);
+      launch_gemm_tn<CfgGrad>(dzt, L.Tp, Vc, ht, L.Tp, L.H, L.T, a.grad_weight + (int64_t)vs0 * L.H, L.H,
+                              a.accumulate_gw, stream);
+    }
+    if (a.grad_hidden) {
+      launch_transpose(a.weight + (int64_t)vs0 * L.H, L.H, Vc, L.H, wt, L.Vs, (Vc + 63) / 64 * 64, stream);
+      launch_gemm_tn<CfgGrad>(dz, L.Vs, L.T, wt, L.Vs, L.H, Vc, a.grad_hidden, L.H, vs0 > 0 ? 1 : 0, stream);
+    }
+  }
+}
+
+}  // namespace lmh

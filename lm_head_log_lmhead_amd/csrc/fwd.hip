@@ -1,0 +1,241 @@
+// fwd.hip — forward kernels of the fused LM-head log-prob.
+//
+// K1 fwd_partials: the logit tile z = W_tile . h_tile^T (vocabulary on the MFMA M axis, tokens on
+//    the N axis, so each lane holds 64 vocabulary entries of one token and the per-token softmax
+//    reduction is mostly in-lane).  Its epilogue reduces every (token, 128-entry vocabulary
+//    chunk) to one record {m, n, b, u}:
+//        m = max z,  n = #{z == m},  b = sum_{z < m} exp(z - m),  u = sum exp(z - m) (z - m)
+//    and stores the label's logit when the label falls in the chunk.  Logits never leave the
+//    registers.  (SkyRL PR #1765 "[megatron] Triton backend for fused LM-head log-prob": the
+//    vocab-tiled online softmax that never materializes per-chunk logits, and the -inf masking of
+//    out-of-bounds vocabulary columns in the tail tile.)
+// K2 fwd_finalize: folds each row's records in a fixed order (64 fixed segments of consecutive
+//    chunks, each folded in ascending order, then the segments in ascending order — a function
+//    of V only) and writes logprob = (z_y - M) - log S, entropy = log S - U/S, lse = M + log S,
+//    with log S = log N + log1p(B/N).  (verl PR #8026, first review: fp32 log_softmax over the
+//    full vocabulary then gather; SkyRL PR #1765, precision-policy commit: logprob 0 for an
+//    out-of-vocabulary label.)
+#include "kernels.hpp"
+
+namespace lmh {
+
+// ---------------------------------------------------------------------------------------------
+// K1: logit tiles + per-chunk records
+// ---------------------------------------------------------------------------------------------
+
+// Logits at vocabulary index >= V (tail tile only) are replaced by this sentinel: it is far
+// below every real logit, so it never reaches the max, and exp2 of its shift underflows to 0, so
+// it adds exactly zero to every sum (0 * d is -0 for finite d).
+constexpr float MASKED_LOGIT = -1.0e30f;
+
+template <int NSUB, bool TAIL>
+__device__ __forceinline__ void fwd_records(f32x16 (&acc)[MSUB][NSUB], int lane, int wave_v0, int tok0, int T,
+                                            int V, const int* __restrict__ labels, f32x4* __restrict__ rec,
+                                            float* __restrict__ zy, int chunk) {
+  const int j = lane & 31;
+  const int hf = lane >> 5;
+  if (TAIL) {
+#pragma unroll
+    for (int m = 0; m < MSUB; ++m)
+#pragma unroll
+      for (int n = 0; n < NSUB; ++n)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (wave_v0 + m * 32 + acc_row(r, lane) >= V) acc[m][n][r] = MASKED_LOGIT;
+  }
+#pragma unroll
+  for (int n = 0; n < NSUB; ++n) {
+    const int tok = tok0 + n * 32 + j;
+    const bool tok_ok = tok < T;
+    const int y = tok_ok ? labels[tok] : -1;
+
+    // pass 1: chunk max over this lane's 64 entries, then across the lane pair (l, l^32), which
+    // together hold the wavefront's 128 entries of this token
+    float mx = acc[0][n][0];
+#pragma unroll
+    for (int m = 0; m < MSUB; ++m)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[m][n][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+
+    // pass 2: count at the max, sum of exp below it, sum of exp * shift (fixed order: m, then r)
+    float cnt = 0.f, b = 0.f, u = 0.f;
+#pragma unroll
+    for (int m = 0; m < MSUB; ++m)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float d = acc[m][n][r] - mx;
+        const float e = __builtin_amdgcn_exp2f(d * LOG2E);
+        const bool at_max = d == 0.f;
+        cnt += at_max ? 1.f : 0.f;
+        b += at_max ? 0.f : e;
+        u = __builtin_fmaf(e, d, u);
+      }
+    // the pair's partial sums: a + b == b + a, so both lanes hold the same bits
+    cnt += __shfl_xor(cnt, 32);
+    b += __shfl_xor(b, 32);
+    u += __shfl_xor(u, 32);
+
+    // label logit: local index w = y - wave_v0 sits in sub-tile w/32, lane half (w/4)%2,
+    // register 4*((w%32)/8) + w%4
+    const int w = y - wave_v0;
+    const bool mine = tok_ok && y < V && (unsigned)w < (unsigned)WAVE_M && ((w >> 2) & 1) == hf;
+    if (__any(mine)) {
+      const int idx = ((w >> 5) << 4) | (((w & 31) >> 3) << 2) | (w & 3);
+      float val = 0.f;
+#pragma unroll
+      for (int m = 0; m < MSUB; ++m)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) val = (idx == m * 16 + r) ? acc[m][n][r] : val;
+      if (mine) zy[tok] = val;
+    }
+    if (hf == 0 && tok_ok) {
+      f32x4 v;
+      v[0] = mx;
+      v[1] = cnt;
+      v[2] = b;
+      v[3] = u;
+      rec[(size_t)chunk * (size_t)T + tok] = v;
+    }
+  }
+}
+
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::NTHREADS) void fwd_partials_kernel(
+    const __bf16* __restrict__ hidden, const __bf16* __restrict__ weight, const int* __restrict__ labels,
+    int T, int H, int V, int n_mt, int n_nt, f32x4* __restrict__ rec, float* __restrict__ zy) {
+  __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
+  int mt, nt;
+  tile_coords<8>(blockIdx.x, gridDim.x, n_mt, n_nt, mt, nt);
+  const int v0 = mt * Cfg::TM;
+  const int t0 = nt * Cfg::TN;
+  f32x16 acc[MSUB][Cfg::NSUB];
+#pragma unroll
+  for (int m = 0; m < MSUB; ++m)
+#pragma unroll
+    for (int n = 0; n < Cfg::NSUB; ++n) acc[m][n] = (f32x16)(0.0f);
+  tile_mainloop<Cfg>(weight + (int64_t)v0 * H, H, min(Cfg::TM, V - v0), hidden + (int64_t)t0 * H, H,
+                     min(Cfg::TN, T - t0), H, lds, acc);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave % Cfg::WM, wn = wave / Cfg::WM;
+  const int wave_v0 = v0 + wm * WAVE_M;
+  if (wave_v0 >= V) return;  // this wavefront's chunk lies wholly past the vocabulary
+  const int tok0 = t0 + wn * Cfg::WAVE_N;
+  const int chunk = wave_v0 / WAVE_M;
+  if (wave_v0 + WAVE_M <= V)
+    fwd_records<Cfg::NSUB, false>(acc, lane, wave_v0, tok0, T, V, labels, rec, zy, chunk);
+  else
+    fwd_records<Cfg::NSUB, true>(acc, lane, wave_v0, tok0, T, V, labels, rec, zy, chunk);
+}
+
+// ---------------------------------------------------------------------------------------------
+// K2: fixed-order fold of the records and the final outputs
+// ---------------------------------------------------------------------------------------------
+
+struct Rec {
+  float m, n, b, u;
+};
+
+// Merge record r into state s (both relative to their own max).  Empty records (n == 0) are the
+// identity.  The three cases keep b and u relative to the larger max, so nothing below the max
+// is ever added to the count n.
+__device__ __forceinline__ Rec fold(Rec s, Rec r) {
+  if (r.n == 0.f) return s;
+  if (s.n == 0.f) return r;
+  if (r.m > s.m) {
+    const float dm = s.m - r.m;
+    const float a = __builtin_amdgcn_exp2f(dm * LOG2E);
+    const float sn = s.b + s.n;
+    Rec o;
+    o.m = r.m;
+    o.n = r.n;
+    o.b = __builtin_fmaf(sn, a, r.b);
+    o.u = __builtin_fmaf(__builtin_fmaf(dm, sn, s.u), a, r.u);
+    return o;
+  }
+  if (r.m == s.m) {
+    s.n += r.n;
+    s.b += r.b;
+    s.u += r.u;
+    return s;
+  }
+  const float dm = r.m - s.m;
+  const float a = __builtin_amdgcn_exp2f(dm * LOG2E);
+  const float rn = r.b + r.n;
+  s.b = __builtin_fmaf(rn, a, s.b);
+  s.u = __builtin_fmaf(__builtin_fmaf(dm, rn, r.u), a, s.u);
+  return s;
+}
+
+constexpr int FIN_TOK = 64;   // tokens per workgroup (one per lane)
+constexpr int FIN_WAVES = 16; // wavefronts per workgroup
+constexpr int FIN_NSEG = 64;  // fixed number of fold segments per row
+
+__global__ __launch_bounds__(FIN_TOK * FIN_WAVES) void fwd_finalize_kernel(
+    const f32x4* __restrict__ rec, const float* __restrict__ zy, const int* __restrict__ labels, int T,
+    int V, int n_c, float* __restrict__ logprob, float* __restrict__ entropy, float* __restrict__ lse) {
+  __shared__ Rec part[FIN_NSEG][FIN_TOK];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int t = blockIdx.x * FIN_TOK + lane;
+  for (int s = w; s < FIN_NSEG; s += FIN_WAVES) {
+    const int lo = (int)((int64_t)s * n_c / FIN_NSEG);
+    const int hi = (int)((int64_t)(s + 1) * n_c / FIN_NSEG);
+    Rec st = {-__builtin_inff(), 0.f, 0.f, 0.f};
+    if (t < T) {
+      for (int c = lo; c < hi; ++c) {
+        const f32x4 v = rec[(size_t)c * (size_t)T + t];
+        st = fold(st, Rec{v[0], v[1], v[2], v[3]});
+      }
+    }
+    part[s][lane] = st;
+  }
+  __syncthreads();
+  if (w != 0 || t >= T) return;
+  Rec st = {-__builtin_inff(), 0.f, 0.f, 0.f};
+#pragma unroll 8
+  for (int s = 0; s < FIN_NSEG; ++s) st = fold(st, part[s][lane]);
+
+  const float logS = logf(st.n) + log1pf(st.b / st.n);
+  const int y = labels[t];
+  const bool in_vocab = y >= 0 && y < V;
+  logprob[t] = in_vocab ? (zy[t] - st.m) - logS : 0.f;
+  if (entropy) entropy[t] = logS - st.u / (st.n + st.b);
+  if (lse) lse[t] = st.m + logS;
+}
+
+// ---------------------------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------------------------
+
+template <class Cfg>
+static void launch_partials_cfg(const FwdArgs& a, hipStream_t stream) {
+  const int n_mt = (a.V + Cfg::TM - 1) / Cfg::TM;
+  const int n_nt = (a.T + Cfg::TN - 1) / Cfg::TN;
+  hipLaunchKernelGGL(fwd_partials_kernel<Cfg>, dim3(n_mt * n_nt), dim3(Cfg::NTHREADS), 0, stream, a.hidden,
+                     a.weight, a.labels, a.T, a.H, a.V, n_mt, n_nt, a.rec, a.zy);
+}
+
+using CfgBig = TileCfg<2, 2, 4>;    // 256 vocab x 256 tokens, 4 wavefronts
+using CfgMid = TileCfg<2, 2, 2>;    // 256 vocab x 128 tokens
+using CfgSmall = TileCfg<2, 1, 1>;  // 256 vocab x 32 tokens, 2 wavefronts
+
+void launch_fwd_partials(const FwdArgs& a, hipStream_t stream) {
+  if (a.T <= 32)
+    launch_partials_cfg<CfgSmall>(a, stream);
+  else if (a.T <= 1024)
+    launch_partials_cfg<CfgMid>(a, stream);
+  else
+    launch_partials_cfg<CfgBig>(a, stream);
+}
+
+void launch_fwd_finalize(const FwdArgs& a, hipStream_t stream) {
+  const int n_c = (a.V + WAVE_M - 1) / WAVE_M;
+  const int nblk = (a.T + FIN_TOK - 1) / FIN_TOK;
+  hipLaunchKernelGGL(fwd_finalize_kernel, dim3(nblk), dim3(FIN_TOK * FIN_WAVES), 0, stream, a.rec, a.zy, a.labels,
+                     a.T, a.V, n_c, a.logprob, a.entropy, a.lse);
+}
+
+}  // namespace lmh

