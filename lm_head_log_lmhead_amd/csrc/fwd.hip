@@ -17,6 +17,21 @@
 //    out-of-vocabulary label.)
 #include "kernels.hpp"
 
+// Build-time tuning knobs for the large-T tile (all choices give the same bits: the per-wavefront
+// vocabulary extent and the MFMA chain are fixed).
+#ifndef LMH_BIG_WN
+#define LMH_BIG_WN 4
+#endif
+#ifndef LMH_BIG_NSUB
+#define LMH_BIG_NSUB 2
+#endif
+#ifndef LMH_BIG_NS
+#define LMH_BIG_NS 4
+#endif
+#ifndef LMH_GROUP_M
+#define LMH_GROUP_M 8
+#endif
+
 namespace lmh {
 
 // ---------------------------------------------------------------------------------------------
@@ -104,9 +119,9 @@ template <class Cfg>
 __global__ __launch_bounds__(Cfg::NTHREADS) void fwd_partials_kernel(
     const __bf16* __restrict__ hidden, const __bf16* __restrict__ weight, const int* __restrict__ labels,
     int T, int H, int V, int n_mt, int n_nt, f32x4* __restrict__ rec, float* __restrict__ zy) {
-  __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
+  __shared__ __attribute__((aligned(1024))) char lds[Cfg::LDS_BYTES];
   int mt, nt;
-  tile_coords<8>(blockIdx.x, gridDim.x, n_mt, n_nt, mt, nt);
+  tile_coords<LMH_GROUP_M>(blockIdx.x, gridDim.x, n_mt, n_nt, mt, nt);
   const int v0 = mt * Cfg::TM;
   const int t0 = nt * Cfg::TN;
   f32x16 acc[MSUB][Cfg::NSUB];
@@ -114,8 +129,8 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void fwd_partials_kernel(
   for (int m = 0; m < MSUB; ++m)
 #pragma unroll
     for (int n = 0; n < Cfg::NSUB; ++n) acc[m][n] = (f32x16)(0.0f);
-  tile_mainloop<Cfg>(weight + (int64_t)v0 * H, H, min(Cfg::TM, V - v0), hidden + (int64_t)t0 * H, H,
-                     min(Cfg::TN, T - t0), H, lds, acc);
+  tile_mainloop2<Cfg>(weight + (int64_t)v0 * H, H, min(Cfg::TM, V - v0), hidden + (int64_t)t0 * H, H,
+                      min(Cfg::TN, T - t0), H, lds, acc);
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -218,9 +233,9 @@ static void launch_partials_cfg(const FwdArgs& a, hipStream_t stream) {
                      a.weight, a.labels, a.T, a.H, a.V, n_mt, n_nt, a.rec, a.zy);
 }
 
-using CfgBig = TileCfg<2, 2, 4>;    // 256 vocab x 256 tokens, 4 wavefronts
-using CfgMid = TileCfg<2, 2, 2>;    // 256 vocab x 128 tokens
-using CfgSmall = TileCfg<2, 1, 1>;  // 256 vocab x 32 tokens, 2 wavefronts
+using CfgBig = PipeCfg<2, LMH_BIG_WN, LMH_BIG_NSUB, LMH_BIG_NS>;  // 256 vocab x 256 tokens, 8 wavefronts
+using CfgMid = PipeCfg<2, 2, 2, 6>;    // 256 vocab x 128 tokens, 4 wavefronts
+using CfgSmall = PipeCfg<2, 1, 1, 8>;  // 256 vocab x 32 tokens, 2 wavefronts, deep prefetch (HBM-bound)
 
 void launch_fwd_partials(const FwdArgs& a, hipStream_t stream) {
   if (a.T <= 32)
