@@ -26,10 +26,18 @@
 #define LMH_BIG_NSUB 2
 #endif
 #ifndef LMH_BIG_NS
-#define LMH_BIG_NS 4
+#define LMH_BIG_NS 2
+#endif
+#ifndef LMH_BIG_BK
+#define LMH_BIG_BK 64
 #endif
 #ifndef LMH_GROUP_M
 #define LMH_GROUP_M 8
+#endif
+// main loop of the large tile: 3 = software-pipelined fragments (tile_mainloop3), 4 = ring with
+// the loads spread between MFMAs (tile_mainloop4, >= 3 stages), 2 = plain ring (tile_mainloop2)
+#ifndef LMH_BIG_LOOP
+#define LMH_BIG_LOOP 3
 #endif
 
 namespace lmh {
@@ -129,8 +137,15 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void fwd_partials_kernel(
   for (int m = 0; m < MSUB; ++m)
 #pragma unroll
     for (int n = 0; n < Cfg::NSUB; ++n) acc[m][n] = (f32x16)(0.0f);
-  tile_mainloop2<Cfg>(weight + (int64_t)v0 * H, H, min(Cfg::TM, V - v0), hidden + (int64_t)t0 * H, H,
-                      min(Cfg::TN, T - t0), H, lds, acc);
+  const __bf16* A = weight + (int64_t)v0 * H;
+  const __bf16* B = hidden + (int64_t)t0 * H;
+  const int rowsA = min(Cfg::TM, V - v0), rowsB = min(Cfg::TN, T - t0);
+  if constexpr (Cfg::LOOP == 4)
+    tile_mainloop4<Cfg>(A, H, rowsA, B, H, rowsB, H, lds, acc);
+  else if constexpr (Cfg::LOOP == 3)
+    tile_mainloop3<Cfg>(A, H, rowsA, B, H, rowsB, H, lds, acc);
+  else
+    tile_mainloop2<Cfg>(A, H, rowsA, B, H, rowsB, H, lds, acc);
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -233,9 +248,19 @@ static void launch_partials_cfg(const FwdArgs& a, hipStream_t stream) {
                      a.weight, a.labels, a.T, a.H, a.V, n_mt, n_nt, a.rec, a.zy);
 }
 
-using CfgBig = PipeCfg<2, LMH_BIG_WN, LMH_BIG_NSUB, LMH_BIG_NS>;  // 256 vocab x 256 tokens, 8 wavefronts
-using CfgMid = PipeCfg<2, 2, 2, 6>;    // 256 vocab x 128 tokens, 4 wavefronts
-using CfgSmall = PipeCfg<2, 1, 1, 8>;  // 256 vocab x 32 tokens, 2 wavefronts, deep prefetch (HBM-bound)
+// Tile configurations, chosen by T.  Each has a 128-entry vocabulary extent per wavefront and the
+// same MFMA chain, so all give the same bits.
+template <class P, int LOOP_>
+struct FwdCfg : P {
+  static constexpr int LOOP = LOOP_;
+};
+// 256 vocab x 256 tokens, 8 wavefronts (2 per SIMD), two stages of K = 64
+using CfgBig = FwdCfg<PipeCfg<2, LMH_BIG_WN, LMH_BIG_NSUB, LMH_BIG_NS, LMH_BIG_BK>, LMH_BIG_LOOP>;
+// 256 vocab x 128 tokens, 4 wavefronts, three stages of K = 64
+using CfgMid = FwdCfg<PipeCfg<2, 2, 2, 3, 64>, 3>;
+// 256 vocab x 32 tokens, 2 wavefronts, eight stages of K = 32 with the loads spread between the
+// MFMAs: the weight stream is HBM-bound here, so deep prefetch matters most
+using CfgSmall = FwdCfg<PipeCfg<2, 1, 1, 8, 32>, 4>;
 
 void launch_fwd_partials(const FwdArgs& a, hipStream_t stream) {
   if (a.T <= 32)

@@ -197,40 +197,45 @@ __device__ __forceinline__ void tile_coords(int bid, int nblk, int n_mt, int n_n
 
 
 // =============================================================================================
-// Main loop v2: a ring of NS LDS stages of BK = 32 filled by direct global -> LDS loads.
+// Main loop v2: a ring of NS LDS stages of BK K-elements filled by direct global -> LDS loads.
 // =============================================================================================
 //
-// Each stage holds the tile's A rows then B rows, 64 bytes (32 bf16) per row, four 16-byte
-// chunks per row with chunk c of row r stored at c ^ ((r >> 2) & 3).  Loads go straight from
-// global memory to LDS (buffer_load_dwordx4 ... lds): one instruction moves 64 lanes x 16 bytes
-// into one contiguous KiB of LDS (16 rows), the lane -> (row, chunk) assignment applying the
-// swizzle.  Stages are filled NS-1 steps ahead, so global latency hides behind NS-1 steps of
-// MFMA work; one barrier per step both publishes the stage and retires the stage it overwrites.
+// Each stage holds the tile's A rows then B rows, BK*2 bytes per row in 16-byte chunks; logical
+// chunk c of row r is stored at c ^ swz2(r).  Loads go straight from global memory to LDS
+// (buffer_load_dwordx4 ... lds): one instruction moves 64 lanes x 16 bytes into one contiguous KiB
+// of LDS, the lane -> (row, chunk) assignment applying the swizzle.  Stages are filled NS-1 steps
+// ahead, so global latency hides behind NS-1 steps of MFMA work; one barrier per step both
+// publishes the stage and retires the stage it overwrites.  With BK = 64 every row contributes a
+// whole 128-byte line per step, so no line is fetched twice into L1.
 //
 // The loads are issued from inline assembly.  The compiler therefore neither counts them nor
 // waits for them; the loop waits with explicit vmcnt values (loads return in order), and the
 // compiler's own waits for other loads stay correct (extra outstanding loads only make a vmcnt
 // wait stricter).  M0 (the LDS destination base) is written inside the same asm block.
 
-constexpr int BK2 = 32;          // K elements per step
-constexpr int ROW2 = BK2 * 2;    // bytes per staged row
-
-template <int WM_, int WN_, int NSUB_, int NS_>
+template <int WM_, int WN_, int NSUB_, int NS_, int BK_ = 64>
 struct PipeCfg {
-  static constexpr int WM = WM_, WN = WN_, NSUB = NSUB_, NS = NS_;
+  static constexpr int WM = WM_, WN = WN_, NSUB = NSUB_, NS = NS_, BK = BK_;
   static constexpr int NWAVES = WM * WN;
   static constexpr int NTHREADS = 64 * NWAVES;
   static constexpr int TM = WAVE_M * WM;
   static constexpr int WAVE_N = 32 * NSUB;
   static constexpr int TN = WAVE_N * WN;
-  static constexpr int A_IPW = TM / 16 / NWAVES;   // DMA instructions per wavefront per step
-  static constexpr int B_IPW = TN / 16 / NWAVES;
-  static constexpr int STAGE_BYTES = (TM + TN) * ROW2;
+  static constexpr int ROW = BK * 2;               // bytes per staged row
+  static constexpr int CPR = BK / 8;               // 16-byte chunks per row
+  static constexpr int RPI = 1024 / ROW;           // rows per DMA instruction
+  static constexpr int KSUB = BK / 16;             // MFMA k-substeps per step
+  static constexpr int A_IPW = TM / RPI / NWAVES;  // DMA instructions per wavefront per step
+  static constexpr int B_IPW = TN / RPI / NWAVES;
+  static constexpr int STAGE_BYTES = (TM + TN) * ROW;
   static constexpr int LDS_BYTES = NS * STAGE_BYTES;
   static constexpr int VMCNT_AHEAD = (NS - 2) * (A_IPW + B_IPW);  // loads allowed in flight
-  static_assert(TM % (16 * NWAVES) == 0 && TN % (16 * NWAVES) == 0 && B_IPW >= 1, "DMA split");
-  static_assert(NS >= 2 && VMCNT_AHEAD <= 63, "vmcnt range");
+  static_assert(BK == 32 || BK == 64, "BK");
+  static_assert(TM % (RPI * NWAVES) == 0 && TN % (RPI * NWAVES) == 0 && B_IPW >= 1, "DMA split");
+  static_assert(NS >= 2 && (NS - 1) * (A_IPW + B_IPW) <= 63, "vmcnt range");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+  // stored chunk of logical chunk c in row r is c ^ swz(r): conflict-free ds_read_b128 of 32 rows
+  __device__ static __forceinline__ int swz(int r) { return BK == 64 ? (r >> 1) & 7 : (r >> 2) & 3; }
 };
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -268,6 +273,7 @@ template <class Cfg>
 __device__ __forceinline__ void tile_mainloop2(const __bf16* __restrict__ A, int64_t lda, int rowsA,
                                                const __bf16* __restrict__ B, int64_t ldb, int rowsB, int K,
                                                char* __restrict__ lds, f32x16 (&acc)[MSUB][Cfg::NSUB]) {
+  constexpr int ROW = Cfg::ROW;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -278,40 +284,50 @@ __device__ __forceinline__ void tile_mainloop2(const __bf16* __restrict__ A, int
   const u32x4 db = make_desc(B, (uint32_t)((int64_t)rowsB * ldb * 2));
   const uint32_t lds0 = lds_addr(lds);
 
-  // DMA lane assignment: lane -> (row lane/4 of the instruction's 16 rows, stored chunk lane%4),
-  // which holds logical chunk (lane%4) ^ ((row >> 2) & 3) = (lane%4) ^ (lane/16).
-  const int dl_row = lane >> 2;
-  const int dl_chunk = (lane & 3) ^ (lane >> 4);
+  // DMA lane assignment: lane -> (row lane / CPR of the instruction's RPI rows, stored chunk
+  // lane % CPR), which holds logical chunk (lane % CPR) ^ swz(row).
+  const int dl_row = lane / Cfg::CPR;
+  const int dl_pc = lane % Cfg::CPR;
   uint32_t a_off[Cfg::A_IPW], b_off[Cfg::B_IPW];
+  int a_lc[Cfg::A_IPW], b_lc[Cfg::B_IPW];
 #pragma unroll
-  for (int i = 0; i < Cfg::A_IPW; ++i)
-    a_off[i] = (uint32_t)(((wave * Cfg::A_IPW + i) * 16 + dl_row) * lda * 2 + dl_chunk * 16);
+  for (int i = 0; i < Cfg::A_IPW; ++i) {
+    const int r = (wave * Cfg::A_IPW + i) * Cfg::RPI + dl_row;
+    a_lc[i] = dl_pc ^ Cfg::swz(r);
+    a_off[i] = (uint32_t)(r * lda * 2 + a_lc[i] * 16);
+  }
 #pragma unroll
-  for (int i = 0; i < Cfg::B_IPW; ++i)
-    b_off[i] = (uint32_t)(((wave * Cfg::B_IPW + i) * 16 + dl_row) * ldb * 2 + dl_chunk * 16);
+  for (int i = 0; i < Cfg::B_IPW; ++i) {
+    const int r = (wave * Cfg::B_IPW + i) * Cfg::RPI + dl_row;
+    b_lc[i] = dl_pc ^ Cfg::swz(r);
+    b_off[i] = (uint32_t)(r * ldb * 2 + b_lc[i] * 16);
+  }
 
-  const int nk = (K + BK2 - 1) / BK2;
+  const int nk = (K + Cfg::BK - 1) / Cfg::BK;
   auto issue = [&](int kt) {
     const int st = kt % Cfg::NS;
-    const bool kin = kt < nk && kt * BK2 + dl_chunk * 8 < K;
-    const uint32_t kb = (uint32_t)kt * ROW2;
+    const bool kt_in = kt < nk;
+    const int k0 = kt * Cfg::BK;
+    const uint32_t kb = (uint32_t)kt * ROW;
     const uint32_t sbase = lds0 + st * Cfg::STAGE_BYTES;
 #pragma unroll
     for (int i = 0; i < Cfg::A_IPW; ++i)
-      dma16(da, kin ? a_off[i] + kb : OOB_OFFSET, sbase + (wave * Cfg::A_IPW + i) * 1024);
+      dma16(da, (kt_in && k0 + a_lc[i] * 8 < K) ? a_off[i] + kb : OOB_OFFSET, sbase + (wave * Cfg::A_IPW + i) * 1024);
 #pragma unroll
     for (int i = 0; i < Cfg::B_IPW; ++i)
-      dma16(db, kin ? b_off[i] + kb : OOB_OFFSET, sbase + Cfg::TM * ROW2 + (wave * Cfg::B_IPW + i) * 1024);
+      dma16(db, (kt_in && k0 + b_lc[i] * 8 < K) ? b_off[i] + kb : OOB_OFFSET,
+            sbase + Cfg::TM * ROW + (wave * Cfg::B_IPW + i) * 1024);
   };
 
-  // Fragment reads: lane reads row (lane & 31) of a 32-row sub-tile, logical chunk 2s + lane/32.
+  // Fragment reads: lane reads row (lane & 31) of a 32-row sub-tile, logical chunk 2s + lane/32;
+  // sub-tile bases are multiples of 32 rows, so the swizzle of the row is swz(lane & 31).
   const int fr = lane & 31;
-  const int fsw = (lane >> 2) & 3;   // (row >> 2) & 3 for rows at multiples of 16 plus fr
-  const int a_frow = (wm * WAVE_M + fr) * ROW2;
-  const int b_frow = Cfg::TM * ROW2 + (wn * Cfg::WAVE_N + fr) * ROW2;
-  int koff[2];
+  const int fsw = Cfg::swz(fr);
+  const int a_frow = (wm * WAVE_M + fr) * ROW;
+  const int b_frow = Cfg::TM * ROW + (wn * Cfg::WAVE_N + fr) * ROW;
+  int koff[Cfg::KSUB];
 #pragma unroll
-  for (int s = 0; s < 2; ++s) koff[s] = (((2 * s) | (lane >> 5)) ^ fsw) << 4;
+  for (int s = 0; s < Cfg::KSUB; ++s) koff[s] = (((2 * s) | (lane >> 5)) ^ fsw) << 4;
 
 #pragma unroll
   for (int p = 0; p < Cfg::NS - 1; ++p) issue(p);
@@ -322,14 +338,14 @@ __device__ __forceinline__ void tile_mainloop2(const __bf16* __restrict__ A, int
     issue(kt + Cfg::NS - 1);
     const char* base = lds + (kt % Cfg::NS) * Cfg::STAGE_BYTES;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    for (int s = 0; s < Cfg::KSUB; ++s) {
       bf16x8 af[MSUB], bfr[Cfg::NSUB];
 #pragma unroll
       for (int m = 0; m < MSUB; ++m)
-        af[m] = *reinterpret_cast<const bf16x8*>(base + a_frow + m * 32 * ROW2 + koff[s]);
+        af[m] = *reinterpret_cast<const bf16x8*>(base + a_frow + m * 32 * ROW + koff[s]);
 #pragma unroll
       for (int n = 0; n < Cfg::NSUB; ++n)
-        bfr[n] = *reinterpret_cast<const bf16x8*>(base + b_frow + n * 32 * ROW2 + koff[s]);
+        bfr[n] = *reinterpret_cast<const bf16x8*>(base + b_frow + n * 32 * ROW + koff[s]);
 #pragma unroll
       for (int m = 0; m < MSUB; ++m)
 #pragma unroll
@@ -338,6 +354,218 @@ __device__ __forceinline__ void tile_mainloop2(const __bf16* __restrict__ A, int
     }
   }
   wait_vmcnt<0>();   // the trailing (out-of-range) loads still write LDS: drain them
+  __syncthreads();
+}
+
+// =============================================================================================
+// Main loop v3: one wavefront per SIMD with a 128 x (32*NSUB) tile, software-pipelined.
+// =============================================================================================
+//
+// Same LDS ring and DMA as v2 with NS = 2 stages of BK = 64, but the fragments are double
+// buffered in registers: the ds_reads of k-substep s+1 are in flight while the MFMAs of substep s
+// run, and the step's barrier sits between the last ds_read of the step and its last MFMAs, so
+// the matrix pipe keeps working across the barrier and the first fragments of the next step load
+// under those MFMAs.  With 128 x 128 per wavefront the LDS read traffic per MFMA is half that of
+// a 128 x 64 wavefront tile, which is what bounds the two-wavefronts-per-SIMD variant.
+//
+// Per accumulator the MFMA sequence is unchanged (k ascending), so results are bit-identical to
+// the other main loops.
+
+template <class Cfg>
+__device__ __forceinline__ void load_frags(const char* base, int a_frow, int b_frow, int koff, bf16x8 (&af)[MSUB],
+                                           bf16x8 (&bfr)[Cfg::NSUB]) {
+#pragma unroll
+  for (int m = 0; m < MSUB; ++m) af[m] = *reinterpret_cast<const bf16x8*>(base + a_frow + m * 32 * Cfg::ROW + koff);
+#pragma unroll
+  for (int n = 0; n < Cfg::NSUB; ++n)
+    bfr[n] = *reinterpret_cast<const bf16x8*>(base + b_frow + n * 32 * Cfg::ROW + koff);
+}
+
+template <class Cfg>
+__device__ __forceinline__ void mfma_block(const bf16x8 (&af)[MSUB], const bf16x8 (&bfr)[Cfg::NSUB],
+                                           f32x16 (&acc)[MSUB][Cfg::NSUB]) {
+#pragma unroll
+  for (int m = 0; m < MSUB; ++m)
+#pragma unroll
+    for (int n = 0; n < Cfg::NSUB; ++n)
+      acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[m], bfr[n], acc[m][n], 0, 0, 0);
+}
+
+template <class Cfg>
+__device__ __forceinline__ void tile_mainloop3(const __bf16* __restrict__ A, int64_t lda, int rowsA,
+                                               const __bf16* __restrict__ B, int64_t ldb, int rowsB, int K,
+                                               char* __restrict__ lds, f32x16 (&acc)[MSUB][Cfg::NSUB]) {
+  constexpr int ROW = Cfg::ROW;
+  constexpr int KSUB = Cfg::KSUB;
+  constexpr int NS = Cfg::NS;
+  constexpr int IPW = Cfg::A_IPW + Cfg::B_IPW;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave % Cfg::WM;
+  const int wn = wave / Cfg::WM;
+
+  const u32x4 da = make_desc(A, (uint32_t)((int64_t)rowsA * lda * 2));
+  const u32x4 db = make_desc(B, (uint32_t)((int64_t)rowsB * ldb * 2));
+  const uint32_t lds0 = lds_addr(lds);
+
+  const int dl_row = lane / Cfg::CPR;
+  const int dl_pc = lane % Cfg::CPR;
+  uint32_t a_off[Cfg::A_IPW], b_off[Cfg::B_IPW];
+  int a_lc[Cfg::A_IPW], b_lc[Cfg::B_IPW];
+#pragma unroll
+  for (int i = 0; i < Cfg::A_IPW; ++i) {
+    const int r = (wave * Cfg::A_IPW + i) * Cfg::RPI + dl_row;
+    a_lc[i] = dl_pc ^ Cfg::swz(r);
+    a_off[i] = (uint32_t)(r * lda * 2 + a_lc[i] * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < Cfg::B_IPW; ++i) {
+    const int r = (wave * Cfg::B_IPW + i) * Cfg::RPI + dl_row;
+    b_lc[i] = dl_pc ^ Cfg::swz(r);
+    b_off[i] = (uint32_t)(r * ldb * 2 + b_lc[i] * 16);
+  }
+  const int nk = (K + Cfg::BK - 1) / Cfg::BK;
+  auto issue = [&](int kt) {  // step kt -> stage kt % NS; steps past the end read zeros
+    const bool kt_in = kt < nk;
+    const int k0 = kt * Cfg::BK;
+    const uint32_t kb = (uint32_t)kt * ROW;
+    const uint32_t sbase = lds0 + (kt % NS) * Cfg::STAGE_BYTES;
+#pragma unroll
+    for (int i = 0; i < Cfg::A_IPW; ++i)
+      dma16(da, (kt_in && k0 + a_lc[i] * 8 < K) ? a_off[i] + kb : OOB_OFFSET, sbase + (wave * Cfg::A_IPW + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < Cfg::B_IPW; ++i)
+      dma16(db, (kt_in && k0 + b_lc[i] * 8 < K) ? b_off[i] + kb : OOB_OFFSET,
+            sbase + Cfg::TM * ROW + (wave * Cfg::B_IPW + i) * 1024);
+  };
+
+  const int fr = lane & 31;
+  const int fsw = Cfg::swz(fr);
+  const int a_frow = (wm * WAVE_M + fr) * ROW;
+  const int b_frow = Cfg::TM * ROW + (wn * Cfg::WAVE_N + fr) * ROW;
+  int koff[KSUB];
+#pragma unroll
+  for (int s = 0; s < KSUB; ++s) koff[s] = (((2 * s) | (lane >> 5)) ^ fsw) << 4;
+
+  // prologue: steps 0..NS-1 in flight, wait for step 0
+#pragma unroll
+  for (int p = 0; p < NS; ++p) issue(p);
+  wait_vmcnt<(NS - 1) * IPW>();
+  __syncthreads();
+  bf16x8 fa[2][MSUB], fb[2][Cfg::NSUB];
+  load_frags<Cfg>(lds, a_frow, b_frow, koff[0], fa[0], fb[0]);
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const char* base = lds + (kt % NS) * Cfg::STAGE_BYTES;
+    const char* nbase = lds + ((kt + 1) % NS) * Cfg::STAGE_BYTES;
+#pragma unroll
+    for (int s = 0; s < KSUB - 1; ++s) {
+      load_frags<Cfg>(base, a_frow, b_frow, koff[s + 1], fa[(s + 1) & 1], fb[(s + 1) & 1]);
+      mfma_block<Cfg>(fa[s & 1], fb[s & 1], acc);
+    }
+    // Every read of stage kt has been issued (the barrier waits for them): publish step kt+1
+    // (its loads were issued NS-1 steps ago) and refill stage kt with step kt+NS.
+    wait_vmcnt<(NS - 2) * IPW>();
+    __syncthreads();
+    issue(kt + NS);
+    if (kt + 1 < nk) load_frags<Cfg>(nbase, a_frow, b_frow, koff[0], fa[0], fb[0]);
+    mfma_block<Cfg>(fa[(KSUB - 1) & 1], fb[(KSUB - 1) & 1], acc);
+  }
+  wait_vmcnt<0>();   // trailing out-of-range loads still write LDS
+  __syncthreads();
+}
+
+// =============================================================================================
+// Main loop v4: the v2 ring with the DMA of each step spread between that step's MFMAs.
+// =============================================================================================
+//
+// Issuing a step's global -> LDS loads in one burst right after the barrier stalls every
+// wavefront at the texture unit (a 1 KiB load instruction takes the unit many cycles) while the
+// matrix pipe idles.  Here the step's NDMA load instructions are interleaved with its NMF MFMAs,
+// one after every NMF/NDMA MFMAs, so address processing overlaps matrix work.  The stage being
+// filled is (kt + NS - 1) % NS, retired by the barrier at the top of step kt; the data of step
+// kt + 1 has NS - 2 further steps of slack, so NS >= 3.
+
+template <class Cfg>
+__device__ __forceinline__ void tile_mainloop4(const __bf16* __restrict__ A, int64_t lda, int rowsA,
+                                               const __bf16* __restrict__ B, int64_t ldb, int rowsB, int K,
+                                               char* __restrict__ lds, f32x16 (&acc)[MSUB][Cfg::NSUB]) {
+  constexpr int ROW = Cfg::ROW;
+  constexpr int KSUB = Cfg::KSUB;
+  constexpr int NS = Cfg::NS;
+  constexpr int NDMA = Cfg::A_IPW + Cfg::B_IPW;
+  constexpr int NMF = KSUB * MSUB * Cfg::NSUB;
+  static_assert(NS >= 3, "v4 main loop needs at least three stages");
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave % Cfg::WM;
+  const int wn = wave / Cfg::WM;
+
+  const u32x4 da = make_desc(A, (uint32_t)((int64_t)rowsA * lda * 2));
+  const u32x4 db = make_desc(B, (uint32_t)((int64_t)rowsB * ldb * 2));
+  const uint32_t lds0 = lds_addr(lds);
+
+  const int dl_row = lane / Cfg::CPR;
+  const int dl_pc = lane % Cfg::CPR;
+  uint32_t d_off[NDMA];
+  int d_lc[NDMA];
+#pragma unroll
+  for (int d = 0; d < NDMA; ++d) {
+    const bool is_a = d < Cfg::A_IPW;
+    const int i = is_a ? d : d - Cfg::A_IPW;
+    const int r = (wave * (is_a ? Cfg::A_IPW : Cfg::B_IPW) + i) * Cfg::RPI + dl_row;
+    d_lc[d] = dl_pc ^ Cfg::swz(r);
+    d_off[d] = (uint32_t)(r * (is_a ? lda : ldb) * 2 + d_lc[d] * 16);
+  }
+  const int nk = (K + Cfg::BK - 1) / Cfg::BK;
+  // load instruction d of step kt (stage kt % NS)
+  auto dma = [&](int d, int kt) {
+    const bool is_a = d < Cfg::A_IPW;
+    const int i = is_a ? d : d - Cfg::A_IPW;
+    const bool ok = kt < nk && kt * Cfg::BK + d_lc[d] * 8 < K;
+    const uint32_t voff = ok ? d_off[d] + (uint32_t)kt * ROW : OOB_OFFSET;
+    const uint32_t dst = lds0 + (kt % NS) * Cfg::STAGE_BYTES +
+                         (is_a ? (wave * Cfg::A_IPW + i) * 1024 : Cfg::TM * ROW + (wave * Cfg::B_IPW + i) * 1024);
+    dma16(is_a ? da : db, voff, dst);
+  };
+
+  const int fr = lane & 31;
+  const int fsw = Cfg::swz(fr);
+  const int a_frow = (wm * WAVE_M + fr) * ROW;
+  const int b_frow = Cfg::TM * ROW + (wn * Cfg::WAVE_N + fr) * ROW;
+  int koff[KSUB];
+#pragma unroll
+  for (int s = 0; s < KSUB; ++s) koff[s] = (((2 * s) | (lane >> 5)) ^ fsw) << 4;
+
+#pragma unroll
+  for (int p = 0; p < NS - 1; ++p)
+#pragma unroll
+    for (int d = 0; d < NDMA; ++d) dma(d, p);
+
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_vmcnt<(NS - 2) * NDMA>();   // this thread's loads of step kt have landed
+    __syncthreads();                 // ... everyone's; and stage (kt - 1) % NS is free again
+    const char* base = lds + (kt % NS) * Cfg::STAGE_BYTES;
+    const int kn = kt + NS - 1;      // the step refilled during this one
+#pragma unroll
+    for (int s = 0; s < KSUB; ++s) {
+      bf16x8 af[MSUB], bfr[Cfg::NSUB];
+      load_frags<Cfg>(base, a_frow, b_frow, koff[s], af, bfr);
+#pragma unroll
+      for (int m = 0; m < MSUB; ++m)
+#pragma unroll
+        for (int n = 0; n < Cfg::NSUB; ++n) {
+          acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[m], bfr[n], acc[m][n], 0, 0, 0);
+          const int q = (s * MSUB + m) * Cfg::NSUB + n;   // MFMA index inside the step
+#pragma unroll
+          for (int d = 0; d < NDMA; ++d)
+            if (d * NMF / NDMA == q) dma(d, kn);
+        }
+    }
+  }
+  wait_vmcnt<0>();   // trailing out-of-range loads still write LDS
   __syncthreads();
 }
 
