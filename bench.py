@@ -3,19 +3,22 @@
 Default workload: the forward (log-prob + entropy) at T=8192 tokens, H=4096, V=152064, bf16
 inputs with the peaked-weight recipe (1% of weight rows x10), synthetic and seeded.
 
-A step is one pass of the whole hot path over the batch: lmhead_logprob_fwd, i.e. the logit-tile
-GEMM with its per-chunk records (stage 1) and the fixed-order fold (stage 2), inputs resident in
-HBM.  W warm-up steps, then K timed steps bracketed by torch.cuda.synchronize(); every stage
-launch is also bracketed by HIP events on the stream the library launches on, which gives the
-dominant kernel's average duration for the roofline.
+A step is one pass of the whole hot path over the batch, inputs resident in HBM: for forward
+workloads lmhead_logprob_fwd, i.e. the logit-tile GEMM with its per-chunk records (stage 1) and
+the fixed-order fold (stage 2); for the forward+backward workload also lmhead_logprob_bwd.
+W warm-up steps, then K timed steps bracketed by torch.cuda.synchronize(); every stage launch is
+also bracketed by HIP events on the stream the library launches on, which gives the dominant
+kernel's average duration for the roofline.
 
 Prints ONE JSON line.  ``--gpus N`` with N > 1 is not supported: this build runs on one GPU.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -30,6 +33,8 @@ import synth  # noqa: E402
 METRIC = "fused LM-head logprob tokens/s + % bf16 MFMA peak, T=8192 H=4096 V=152064"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+CSRC = os.path.join(ROOT, "lm_head_log_lmhead_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
 
 
 def parse():
@@ -43,6 +48,28 @@ def parse():
     p.add_argument("--copy-bytes", type=int, default=0,
                    help="also run a plain device copy of this many bytes (counter calibration)")
     return p.parse_args()
+
+
+def kernel_sources_digest() -> str:
+    h = hashlib.sha256()
+    for f in ("tile_gemm.hpp", "fwd.hip", "kernels.hpp"):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the dominant kernel from the committed counter summary, if that
+    summary was taken on the current kernel sources (else None)."""
+    path = os.path.join(PROFILES, f"fwd_partials_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"sources digest:\s*`?([0-9a-f]{16})", text)
+    t = re.search(r"traffic bytes per launch:\s*`?([0-9.eE+]+)", text)
+    if not m or not t or m.group(1) != kernel_sources_digest():
+        return None
+    return float(t.group(1))
 
 
 def cpu_baseline(x, rows: int, name: str):
@@ -83,6 +110,11 @@ def main():
     ent = torch.empty(T, dtype=torch.float32, device=dev) if wl.entropy else None
     lse = torch.empty(T, dtype=torch.float32, device=dev)
     ws = torch.empty(lmh.lmhead_logprob_fwd_workspace_size(T, H, V), dtype=torch.uint8, device=dev)
+    if wl.backward:
+        g = x.grad.to(dev)
+        gh = torch.empty((T, H), dtype=torch.float32, device=dev)
+        gw = torch.empty((V, H), dtype=torch.float32, device=dev)
+        wsb = torch.empty(lmh.lmhead_logprob_bwd_workspace_size(T, H, V), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
     if a.copy_bytes:
@@ -91,6 +123,8 @@ def main():
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
+
+    nev = 4 if wl.backward else 3
 
     def step(evs=None):
         if evs is not None:
@@ -101,12 +135,16 @@ def main():
         lmh.lmhead_logprob_fwd_finalize(y, T, H, V, lp, ent, lse, ws, stream)
         if evs is not None:
             evs[2].record(stream)
+        if wl.backward:
+            lmh.lmhead_logprob_bwd(h, w, y, g, lse, gh, gw, False, wsb, stream)
+            if evs is not None:
+                evs[3].record(stream)
 
     print(f"[bench] warmup {a.warmup}", file=sys.stderr, flush=True)
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(a.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(a.steps)]
     print(f"[bench] timing {a.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -116,9 +154,22 @@ def main():
     wall = time.perf_counter() - t0
     k1 = sum(e[0].elapsed_time(e[1]) for e in evs) / a.steps       # ms, stage 1 (logit tiles + records)
     k2 = sum(e[1].elapsed_time(e[2]) for e in evs) / a.steps       # ms, stage 2 (fold)
+    kb = sum(e[2].elapsed_time(e[3]) for e in evs) / a.steps if wl.backward else 0.0
     ms = wall * 1e3 / a.steps
-    flops = 2.0 * T * H * V
-    k1_tflops = flops / (k1 * 1e-3) / 1e12
+    fwd_flops = 2.0 * T * H * V
+    flops = fwd_flops * (4.0 if wl.backward else 1.0)   # backward: recompute + two gradient GEMMs
+    alg_bytes = 2.0 * V * H + 2.0 * T * H + 12.0 * T     # W once, h once, labels + outputs
+    k1_tflops = fwd_flops / (k1 * 1e-3) / 1e12
+    k1_gbs = alg_bytes / (k1 * 1e-3) / 1e9
+    # W (2VH bytes) streamed once for 2TVH flops: T flop/B; below the ridge the kernel is HBM-bound
+    hbm_bound = T < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    traffic = measured_traffic(a.workload)
+    if hbm_bound:
+        roof = {"bound": "hbm", "kernel": "fwd_partials_kernel", "achieved": k1_gbs, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": k1_gbs / PEAK_HBM_GBS, "traffic": traffic}
+    else:
+        roof = {"bound": "mfma", "kernel": "fwd_partials_kernel", "achieved": k1_tflops, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": k1_tflops / PEAK_BF16_TFLOPS, "traffic": traffic}
     out = {
         "metric": METRIC,
         "value": T / (ms * 1e-3),
@@ -132,21 +183,17 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": a.workload, "T": T, "H": H, "V": V, "entropy": bool(wl.entropy)},
+        "config": {"workload": a.workload, "T": T, "H": H, "V": V, "entropy": bool(wl.entropy),
+                   "backward": bool(wl.backward)},
         "tflops": flops / (ms * 1e-3) / 1e12,
         "pct_bf16_mfma_peak": 100.0 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-        "stage_ms": {"fwd_partials": k1, "fwd_finalize": k2},
-        "roofline": {
-            "bound": "mfma",
-            "kernel": "fwd_partials_kernel",
-            "achieved": k1_tflops,
-            "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": k1_tflops / PEAK_BF16_TFLOPS,
-            "traffic": None,
-        },
-        "hbm_gbs_algorithmic": (2.0 * V * H + 2.0 * T * H + 12.0 * T) / (ms * 1e-3) / 1e9,
+        "stage_ms": {"fwd_partials": k1, "fwd_finalize": k2, **({"bwd": kb} if wl.backward else {})},
+        "roofline": roof,
+        "hbm_gbs_algorithmic": alg_bytes / (k1 * 1e-3) / 1e9,
+        "kernel_sources_digest": kernel_sources_digest(),
     }
+    if wl.backward:
+        out["bwd_tflops"] = 6.0 * T * H * V / (kb * 1e-3) / 1e12
     if a.cpu_sample_rows > 0:
         print(f"[bench] timing the CPU oracle on {a.cpu_sample_rows} rows", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(x, min(a.cpu_sample_rows, T), a.workload)
