@@ -33,7 +33,7 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void bwd_dz_kernel(
     int Vs, int n_mt, int n_nt, __bf16* __restrict__ dz) {
   constexpr int STAGE_OUT = Cfg::NWAVES * Cfg::WAVE_N * DZ_PITCH;
   constexpr int LDS = Cfg::LDS_BYTES > STAGE_OUT ? Cfg::LDS_BYTES : STAGE_OUT;
-  __shared__ __attribute__((aligned(16))) char lds[LDS];
+  __shared__ __attribute__((aligned(1024))) char lds[LDS];
   int mt, nt;
   tile_coords<8>(blockIdx.x, gridDim.x, n_mt, n_nt, mt, nt);
   const int v0 = mt * Cfg::TM;  // local vocabulary row inside the step
@@ -43,8 +43,8 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void bwd_dz_kernel(
   for (int m = 0; m < MSUB; ++m)
 #pragma unroll
     for (int n = 0; n < Cfg::NSUB; ++n) acc[m][n] = (f32x16)(0.0f);
-  tile_mainloop<Cfg>(weight + (int64_t)(vs0 + v0) * H, H, min(Cfg::TM, Vc - v0), hidden + (int64_t)t0 * H, H,
-                     min(Cfg::TN, T - t0), H, lds, acc);
+  tile_mainloop3<Cfg>(weight + (int64_t)(vs0 + v0) * H, H, min(Cfg::TM, Vc - v0), hidden + (int64_t)t0 * H, H,
+                      min(Cfg::TN, T - t0), H, lds, acc);
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -143,16 +143,27 @@ static void launch_transpose(const __bf16* src, int64_t ld_src, int R, int C, __
 }
 
 // ---------------------------------------------------------------------------------------------
-// K4 / K5: C[M x N] fp32 = (accumulate ? C : 0) + A[M x K] . B[N x K]^T
+// K4 / K5: C[M x N] fp32 = (accumulate ? C : 0) + A[M x K] . B[N x K]^T, two problems per launch
 // ---------------------------------------------------------------------------------------------
 
+struct GemmProblem {
+  const __bf16* A;
+  int64_t lda;
+  int M;
+  const __bf16* B;
+  int64_t ldb;
+  int N;
+  int K;
+  float* C;
+  int64_t ldc;
+  int accumulate;
+  int n_mt, n_nt;
+};
+
 template <class Cfg>
-__global__ __launch_bounds__(Cfg::NTHREADS) void gemm_tn_f32_kernel(
-    const __bf16* __restrict__ A, int64_t lda, int M, const __bf16* __restrict__ B, int64_t ldb, int N, int K,
-    float* __restrict__ C, int64_t ldc, int accumulate, int n_mt, int n_nt) {
-  __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
+__device__ __forceinline__ void gemm_tn_tile(const GemmProblem& p, int bid, int nblk, char* lds) {
   int mt, nt;
-  tile_coords<8>(blockIdx.x, gridDim.x, n_mt, n_nt, mt, nt);
+  tile_coords<8>(bid, nblk, p.n_mt, p.n_nt, mt, nt);
   const int m0 = mt * Cfg::TM;
   const int n0 = nt * Cfg::TN;
   const int lane = threadIdx.x & 63;
@@ -161,6 +172,7 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void gemm_tn_f32_kernel(
   const int rbase = m0 + wm * WAVE_M;
   const int cbase = n0 + wn * Cfg::WAVE_N + (lane & 31);
 
+  // the accumulator starts at C when accumulating, so the MFMA chain continues across calls
   f32x16 acc[MSUB][Cfg::NSUB];
 #pragma unroll
   for (int m = 0; m < MSUB; ++m)
@@ -170,11 +182,11 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void gemm_tn_f32_kernel(
       for (int r = 0; r < 16; ++r) {
         const int row = rbase + m * 32 + acc_row(r, lane);
         const int col = cbase + n * 32;
-        acc[m][n][r] = (accumulate && row < M && col < N) ? C[(int64_t)row * ldc + col] : 0.f;
+        acc[m][n][r] = (p.accumulate && row < p.M && col < p.N) ? p.C[(int64_t)row * p.ldc + col] : 0.f;
       }
 
-  tile_mainloop<Cfg>(A + (int64_t)m0 * lda, lda, min(Cfg::TM, M - m0), B + (int64_t)n0 * ldb, ldb,
-                     min(Cfg::TN, N - n0), K, lds, acc);
+  tile_mainloop3<Cfg>(p.A + (int64_t)m0 * p.lda, p.lda, min(Cfg::TM, p.M - m0), p.B + (int64_t)n0 * p.ldb, p.ldb,
+                      min(Cfg::TN, p.N - n0), p.K, lds, acc);
 
 #pragma unroll
   for (int m = 0; m < MSUB; ++m)
@@ -184,17 +196,39 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void gemm_tn_f32_kernel(
       for (int r = 0; r < 16; ++r) {
         const int row = rbase + m * 32 + acc_row(r, lane);
         const int col = cbase + n * 32;
-        if (row < M && col < N) C[(int64_t)row * ldc + col] = acc[m][n][r];
+        if (row < p.M && col < p.N) p.C[(int64_t)row * p.ldc + col] = acc[m][n][r];
       }
 }
 
+// Workgroups [0, nblk0) run problem 0 and [nblk0, grid) problem 1; nblk0 is padded to a multiple
+// of 8 (padding workgroups exit at once) so both problems keep the XCD-aware tile order.
 template <class Cfg>
-static void launch_gemm_tn(const __bf16* A, int64_t lda, int M, const __bf16* B, int64_t ldb, int N, int K, float* C,
-                           int64_t ldc, int accumulate, hipStream_t stream) {
-  const int n_mt = (M + Cfg::TM - 1) / Cfg::TM;
-  const int n_nt = (N + Cfg::TN - 1) / Cfg::TN;
-  hipLaunchKernelGGL(gemm_tn_f32_kernel<Cfg>, dim3(n_mt * n_nt), dim3(Cfg::NTHREADS), 0, stream, A, lda, M, B, ldb,
-                     N, K, C, ldc, accumulate, n_mt, n_nt);
+__global__ __launch_bounds__(Cfg::NTHREADS) void gemm_tn_f32_kernel(GemmProblem p0, GemmProblem p1, int nblk0,
+                                                                    int used0) {
+  __shared__ __attribute__((aligned(1024))) char lds[Cfg::LDS_BYTES];
+  const int bid = blockIdx.x;
+  if (bid < nblk0) {
+    if (bid < used0) gemm_tn_tile<Cfg>(p0, bid, used0, lds);
+  } else {
+    gemm_tn_tile<Cfg>(p1, bid - nblk0, gridDim.x - nblk0, lds);
+  }
+}
+
+template <class Cfg>
+static GemmProblem make_problem(const __bf16* A, int64_t lda, int M, const __bf16* B, int64_t ldb, int N, int K,
+                                float* C, int64_t ldc, int accumulate) {
+  GemmProblem p{A, lda, M, B, ldb, N, K, C, ldc, accumulate, (M + Cfg::TM - 1) / Cfg::TM, (N + Cfg::TN - 1) / Cfg::TN};
+  return p;
+}
+
+// Launches one or two problems (p1.M == 0: none) in a single grid.
+template <class Cfg>
+static void launch_gemm_tn(const GemmProblem& p0, const GemmProblem& p1, hipStream_t stream) {
+  const int used0 = p0.M > 0 ? p0.n_mt * p0.n_nt : 0;
+  const int n1 = p1.M > 0 ? p1.n_mt * p1.n_nt : 0;
+  const int nblk0 = (used0 + 7) / 8 * 8;
+  if (used0 + n1 == 0) return;
+  hipLaunchKernelGGL(gemm_tn_f32_kernel<Cfg>, dim3(nblk0 + n1), dim3(Cfg::NTHREADS), 0, stream, p0, p1, nblk0, used0);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -224,8 +258,9 @@ BwdLayout bwd_layout(int64_t T, int64_t H, int64_t V) {
   return L;
 }
 
-using CfgDz = TileCfg<2, 2, 4>;
-using CfgGrad = TileCfg<2, 2, 4>;
+// 256 x 256 tiles, 8 wavefronts (2 per SIMD), two LDS stages of K = 64, main loop 3
+using CfgDz = PipeCfg<2, 4, 2, 2, 64>;
+using CfgGrad = PipeCfg<2, 4, 2, 2, 64>;
 
 void launch_bwd(const BwdArgs& a, hipStream_t stream) {
   const BwdLayout& L = a.L;
@@ -245,15 +280,17 @@ void launch_bwd(const BwdArgs& a, hipStream_t stream) {
                          a.weight, a.labels, a.grad, a.lse, L.T, L.H, L.V, vs0, Vc, L.Vs, n_mt, n_nt, dz);
     }
     const int Vc8 = (Vc + 7) / 8 * 8;  // dz columns past Vc inside the written tiles are zeros
+    GemmProblem pw{}, ph{};
     if (a.grad_weight) {
       launch_transpose(dz, L.Vs, L.T, Vc8, dzt, L.Tp, L.Tp, stream);
-      launch_gemm_tn<CfgGrad>(dzt, L.Tp, Vc, ht, L.Tp, L.H, L.T, a.grad_weight + (int64_t)vs0 * L.H, L.H,
-                              a.accumulate_gw, stream);
+      pw = make_problem<CfgGrad>(dzt, L.Tp, Vc, ht, L.Tp, L.H, L.T, a.grad_weight + (int64_t)vs0 * L.H, L.H,
+                                 a.accumulate_gw);
     }
     if (a.grad_hidden) {
       launch_transpose(a.weight + (int64_t)vs0 * L.H, L.H, Vc, L.H, wt, L.Vs, (Vc + 63) / 64 * 64, stream);
-      launch_gemm_tn<CfgGrad>(dz, L.Vs, L.T, wt, L.Vs, L.H, Vc, a.grad_hidden, L.H, vs0 > 0 ? 1 : 0, stream);
+      ph = make_problem<CfgGrad>(dz, L.Vs, L.T, wt, L.Vs, L.H, Vc, a.grad_hidden, L.H, vs0 > 0 ? 1 : 0);
     }
+    launch_gemm_tn<CfgGrad>(pw, ph, stream);
   }
 }
 

@@ -11,7 +11,7 @@ namespace lmh {
 
 // Vocabulary width of one forward record (one wavefront's M extent).
 constexpr int VOCAB_CHUNK = WAVE_M;
-// Vocabulary rows per backward step (a multiple of 256 and of BK).  grad_hidden does not depend on
+// Vocabulary rows per backward step (a multiple of the 256-row tile and of the K step).  grad_hidden does not depend on
 // it bit-wise: each step continues the previous step's MFMA accumulation chain.
 constexpr int BWD_VOCAB_STEP = 16384;
 
