@@ -11,8 +11,9 @@ namespace lmh {
 
 // Vocabulary width of one forward record (one wavefront's M extent).
 constexpr int VOCAB_CHUNK = WAVE_M;
-// Vocabulary rows per backward step (a multiple of the 256-row tile and of the K step).  grad_hidden does not depend on
-// it bit-wise: each step continues the previous step's MFMA accumulation chain.
+// Vocabulary rows per backward step (a multiple of the 256-row tile and of the K step).
+// grad_hidden does not depend on it bit-wise: each step continues the previous step's MFMA
+// accumulation chain.
 constexpr int BWD_VOCAB_STEP = 16384;
 
 struct FwdArgs {

@@ -220,14 +220,15 @@ __device__ __forceinline__ void tile_mainloop2(const __bf16* __restrict__ A, int
 }
 
 // =============================================================================================
-// Main loop v3: one wavefront per SIMD with a 128 x (32*NSUB) tile, software-pipelined.
+// Main loop v3: the v2 ring with software-pipelined fragments.
 // =============================================================================================
 //
-// Same LDS ring and DMA as v2, but the fragments are double buffered in registers: the ds_reads of k-substep s+1 are in flight while the MFMAs of substep s
-// run, and the step's barrier sits between the last ds_read of the step and its last MFMAs, so
-// the matrix pipe keeps working across the barrier and the first fragments of the next step load
-// under those MFMAs.  With 128 x 128 per wavefront the LDS read traffic per MFMA is half that of
-// a 128 x 64 wavefront tile, which is what bounds the two-wavefronts-per-SIMD variant.
+// The fragments are double buffered in registers: the ds_reads of k-substep s+1 are in flight
+// while the MFMAs of substep s run, and the step's barrier sits between the last ds_read of the
+// step and its last MFMAs, so the matrix pipe keeps working across the barrier and the first
+// fragments of the next step load under those MFMAs.  Stage kt is refilled with step kt+NS right
+// after that barrier (every read of stage kt has been issued by then), so NS = 2 stages of K = 64
+// already give each load one step of slack.  Used with one or two wavefronts per SIMD.
 //
 // Per accumulator the MFMA sequence is unchanged (k ascending), so results are bit-identical to
 // the other main loops.
