@@ -34,6 +34,32 @@
 #ifndef LMH_GROUP_M
 #define LMH_GROUP_M 8
 #endif
+// small-T tile (T <= 32): wavefronts along the vocabulary, stages, K step, main loop
+#ifndef LMH_SMALL_WM
+#define LMH_SMALL_WM 2
+#endif
+#ifndef LMH_SMALL_NS
+#define LMH_SMALL_NS 4
+#endif
+#ifndef LMH_SMALL_BK
+#define LMH_SMALL_BK 64
+#endif
+#ifndef LMH_SMALL_LOOP
+#define LMH_SMALL_LOOP 4
+#endif
+// 32 < T <= 64 tile
+#ifndef LMH_S64_WM
+#define LMH_S64_WM 2
+#endif
+#ifndef LMH_S64_NS
+#define LMH_S64_NS 4
+#endif
+#ifndef LMH_S64_BK
+#define LMH_S64_BK 64
+#endif
+#ifndef LMH_S64_LOOP
+#define LMH_S64_LOOP 4
+#endif
 // main loop of the large tile: 3 = software-pipelined fragments (tile_mainloop3), 4 = ring with
 // the loads spread between MFMAs (tile_mainloop4, >= 3 stages), 2 = plain ring (tile_mainloop2)
 #ifndef LMH_BIG_LOOP
@@ -207,21 +233,40 @@ __global__ __launch_bounds__(FIN_TOK * FIN_WAVES) void fwd_finalize_kernel(
     const f32x4* __restrict__ rec, const float* __restrict__ zy, const int* __restrict__ labels, int T,
     int V, int n_c, float* __restrict__ logprob, float* __restrict__ entropy, float* __restrict__ lse) {
   __shared__ Rec part[FIN_NSEG][FIN_TOK];
+  constexpr int SEG_PER_WAVE = FIN_NSEG / FIN_WAVES;
+  constexpr int BATCH = 4;  // records per segment loaded before folding: 16 loads in flight
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int t = blockIdx.x * FIN_TOK + lane;
-  for (int s = w; s < FIN_NSEG; s += FIN_WAVES) {
-    const int lo = (int)((int64_t)s * n_c / FIN_NSEG);
-    const int hi = (int)((int64_t)(s + 1) * n_c / FIN_NSEG);
-    Rec st = {-__builtin_inff(), 0.f, 0.f, 0.f};
-    if (t < T) {
-      for (int c = lo; c < hi; ++c) {
-        const f32x4 v = rec[(size_t)c * (size_t)T + t];
-        st = fold(st, Rec{v[0], v[1], v[2], v[3]});
-      }
-    }
-    part[s][lane] = st;
+  const bool t_ok = t < T;
+  int lo[SEG_PER_WAVE], len[SEG_PER_WAVE];
+  Rec seg[SEG_PER_WAVE];
+  int maxlen = 0;
+#pragma unroll
+  for (int j = 0; j < SEG_PER_WAVE; ++j) {
+    const int s = w + FIN_WAVES * j;
+    lo[j] = (int)((int64_t)s * n_c / FIN_NSEG);
+    len[j] = (int)((int64_t)(s + 1) * n_c / FIN_NSEG) - lo[j];
+    maxlen = max(maxlen, len[j]);
+    seg[j] = Rec{-__builtin_inff(), 0.f, 0.f, 0.f};
   }
+  // Each segment is folded in ascending chunk order; the loads of a batch are all issued first.
+  for (int b = 0; b < maxlen; b += BATCH) {
+    f32x4 r[SEG_PER_WAVE][BATCH];
+#pragma unroll
+    for (int j = 0; j < SEG_PER_WAVE; ++j)
+#pragma unroll
+      for (int i = 0; i < BATCH; ++i) {
+        const int c = b + i;
+        r[j][i] = (t_ok && c < len[j]) ? rec[(size_t)(lo[j] + c) * (size_t)T + t] : (f32x4)(0.f);
+      }
+#pragma unroll
+    for (int j = 0; j < SEG_PER_WAVE; ++j)
+#pragma unroll
+      for (int i = 0; i < BATCH; ++i) seg[j] = fold(seg[j], Rec{r[j][i][0], r[j][i][1], r[j][i][2], r[j][i][3]});
+  }
+#pragma unroll
+  for (int j = 0; j < SEG_PER_WAVE; ++j) part[w + FIN_WAVES * j][lane] = seg[j];
   __syncthreads();
   if (w != 0 || t >= T) return;
   Rec st = {-__builtin_inff(), 0.f, 0.f, 0.f};
@@ -258,13 +303,17 @@ struct FwdCfg : P {
 using CfgBig = FwdCfg<PipeCfg<2, LMH_BIG_WN, LMH_BIG_NSUB, LMH_BIG_NS, LMH_BIG_BK>, LMH_BIG_LOOP>;
 // 256 vocab x 128 tokens, 4 wavefronts, three stages of K = 64
 using CfgMid = FwdCfg<PipeCfg<2, 2, 2, 3, 64>, 3>;
-// 256 vocab x 32 tokens, 2 wavefronts, eight stages of K = 32 with the loads spread between the
-// MFMAs: the weight stream is HBM-bound here, so deep prefetch matters most
-using CfgSmall = FwdCfg<PipeCfg<2, 1, 1, 8, 32>, 4>;
+// T <= 32: 256 vocab x 32 tokens, 2 wavefronts, four stages of K = 64 with the loads spread between
+// the MFMAs: the weight stream is HBM-bound here, so deep prefetch matters most
+using CfgSmall = FwdCfg<PipeCfg<LMH_SMALL_WM, 1, 1, LMH_SMALL_NS, LMH_SMALL_BK>, LMH_SMALL_LOOP>;
+// 32 < T <= 64: 256 vocab x 64 tokens, 2 wavefronts, four stages of K = 64 (160 KB of LDS)
+using CfgS64 = FwdCfg<PipeCfg<LMH_S64_WM, 1, 2, LMH_S64_NS, LMH_S64_BK>, LMH_S64_LOOP>;
 
 void launch_fwd_partials(const FwdArgs& a, hipStream_t stream) {
   if (a.T <= 32)
     launch_partials_cfg<CfgSmall>(a, stream);
+  else if (a.T <= 64)
+    launch_partials_cfg<CfgS64>(a, stream);
   else if (a.T <= 1024)
     launch_partials_cfg<CfgMid>(a, stream);
   else
