@@ -63,7 +63,7 @@
 // main loop of the large tile: 3 = software-pipelined fragments (tile_mainloop3), 4 = ring with
 // the loads spread between MFMAs (tile_mainloop4, >= 3 stages), 2 = plain ring (tile_mainloop2)
 #ifndef LMH_BIG_LOOP
-#define LMH_BIG_LOOP 3
+#define LMH_BIG_LOOP 7
 #endif
 
 namespace lmh {
@@ -166,7 +166,13 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void fwd_partials_kernel(
   const __bf16* A = weight + (int64_t)v0 * H;
   const __bf16* B = hidden + (int64_t)t0 * H;
   const int rowsA = min(Cfg::TM, V - v0), rowsB = min(Cfg::TN, T - t0);
-  if constexpr (Cfg::LOOP == 4)
+  if constexpr (Cfg::LOOP == 7)
+    tile_mainloop7<Cfg>(A, H, rowsA, B, H, rowsB, H, lds, acc);
+  else if constexpr (Cfg::LOOP == 6)
+    tile_mainloop6<Cfg>(A, H, rowsA, B, H, rowsB, H, lds, acc);
+  else if constexpr (Cfg::LOOP == 5)
+    tile_mainloop5<Cfg>(A, H, rowsA, B, H, rowsB, H, lds, acc);
+  else if constexpr (Cfg::LOOP == 4)
     tile_mainloop4<Cfg>(A, H, rowsA, B, H, rowsB, H, lds, acc);
   else if constexpr (Cfg::LOOP == 3)
     tile_mainloop3<Cfg>(A, H, rowsA, B, H, rowsB, H, lds, acc);
@@ -298,8 +304,12 @@ static void launch_partials_cfg(const FwdArgs& a, hipStream_t stream) {
 template <class P, int LOOP_>
 struct FwdCfg : P {
   static constexpr int LOOP = LOOP_;
+  // the v7 loop keeps three A slots and two B slots of one K step each
+  static constexpr int LDS_BYTES = LOOP_ == 7 ? 5 * 256 * P::ROW : P::LDS_BYTES;
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
-// 256 vocab x 256 tokens, 8 wavefronts (2 per SIMD), two stages of K = 64
+// 256 vocab x 256 tokens, 8 wavefronts (2 per SIMD) in two groups that alternate between loads and
+// MFMAs, K = 64 steps, three A slots and two B slots (160 KB of LDS)
 using CfgBig = FwdCfg<PipeCfg<2, LMH_BIG_WN, LMH_BIG_NSUB, LMH_BIG_NS, LMH_BIG_BK>, LMH_BIG_LOOP>;
 // 256 vocab x 128 tokens, 4 wavefronts, three stages of K = 64
 using CfgMid = FwdCfg<PipeCfg<2, 2, 2, 3, 64>, 3>;

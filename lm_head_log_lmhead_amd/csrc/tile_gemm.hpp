@@ -431,4 +431,348 @@ __device__ __forceinline__ void tile_mainloop4(const __bf16* __restrict__ A, int
   __syncthreads();
 }
 
+// =============================================================================================
+// Main loop v5: two groups of four wavefronts in ping-pong.
+// =============================================================================================
+//
+// Eight wavefronts, two per SIMD (wavefronts w and w+4 share SIMD w % 4).  Group 0 = wavefronts
+// 0-3, group 1 = 4-7; each has one wavefront per SIMD.  Every wavefront runs the same sequence
+// "load the fragments of step k from LDS | barrier | 32 MFMAs of step k | barrier", but group 1
+// starts one barrier later, so in every phase one group issues MFMAs back to back from registers
+// while the other reads LDS: each SIMD's matrix pipe is fed by one wavefront per phase without
+// waiting on LDS.  (Hardware barriers count arrivals, so the groups may sit at different barrier
+// instructions as long as every wavefront executes the same number of them.)
+//
+//   phase 2k:    group 0 issues the global -> LDS loads of step k+1 into stage (k+1) % 2 (last read
+//                in phases 2k-2 and 2k-1) and reads the fragments of step k; group 1 computes k-1
+//   phase 2k+1:  group 0 computes step k, then waits for its loads of step k+1;
+//                group 1 reads the fragments of step k
+//
+// Per accumulator the MFMA sequence is unchanged (k ascending), so results are bit-identical to the
+// other main loops.
+
+template <class Cfg>
+__device__ __forceinline__ void tile_mainloop5(const __bf16* __restrict__ A, int64_t lda, int rowsA,
+                                               const __bf16* __restrict__ B, int64_t ldb, int rowsB, int K,
+                                               char* __restrict__ lds, f32x16 (&acc)[MSUB][Cfg::NSUB]) {
+  static_assert(Cfg::NWAVES == 8 && Cfg::WM == 2 && Cfg::NS == 2 && Cfg::BK == 64, "v5: 8 wavefronts, 2 x K64");
+  constexpr int ROW = Cfg::ROW;                   // 128 bytes
+  constexpr int NBLK = (Cfg::TM + Cfg::TN) / 8;   // 8-row DMA blocks per stage
+  constexpr int DPW = NBLK / 4;                   // DMA instructions per group-0 wavefront per step
+  static_assert(Cfg::TM / 8 == 2 * DPW && Cfg::TN / 8 == 2 * DPW && DPW <= 31, "v5 DMA split");
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int group = wave >> 2;
+  const int gw = wave & 3;
+  const int wm = wave % Cfg::WM;
+  const int wn = wave / Cfg::WM;
+
+  // ---- global -> LDS (group 0): wavefronts 0,1 load the A rows, 2,3 the B rows
+  const bool dma_a = gw < 2;
+  const u32x4 desc = dma_a ? make_desc(A, (uint32_t)((int64_t)rowsA * lda * 2))
+                           : make_desc(B, (uint32_t)((int64_t)rowsB * ldb * 2));
+  const int64_t ld = dma_a ? lda : ldb;
+  const int blk0 = (gw & 1) * DPW;                // first 8-row block (even: block parity = i parity)
+  const uint32_t lds0 = lds_addr(lds);
+  const uint32_t part = dma_a ? 0u : (uint32_t)(Cfg::TM * ROW);
+  const int dl_row = lane >> 3;
+  const int dl_pc = lane & 7;
+  // the stored chunk of row r is c ^ ((r >> 1) & 7), r = 8 * (blk0 + i) + dl_row
+  const int lc_even = dl_pc ^ (dl_row >> 1);
+  const int lc_odd = dl_pc ^ (4 + (dl_row >> 1));
+  const uint32_t row_off = (uint32_t)((blk0 * 8 + dl_row) * ld * 2);
+  const uint32_t blk_stride = (uint32_t)(8 * ld * 2);
+  const int nk = (K + Cfg::BK - 1) / Cfg::BK;
+  auto dma_step = [&](int kt) {
+    const bool kt_in = kt < nk;
+    const int k0 = kt * Cfg::BK;
+    const bool ok_even = kt_in && k0 + lc_even * 8 < K;
+    const bool ok_odd = kt_in && k0 + lc_odd * 8 < K;
+    const uint32_t ve = row_off + lc_even * 16 + (uint32_t)kt * ROW;
+    const uint32_t vo = row_off + lc_odd * 16 + (uint32_t)kt * ROW;
+    const uint32_t sbase = lds0 + (kt & 1) * Cfg::STAGE_BYTES + part + blk0 * 1024;
+#pragma unroll
+    for (int i = 0; i < DPW; ++i) {
+      const bool ok = (i & 1) ? ok_odd : ok_even;
+      const uint32_t voff = ((i & 1) ? vo : ve) + (uint32_t)i * blk_stride;
+      dma16(desc, ok ? voff : OOB_OFFSET, sbase + i * 1024);
+    }
+  };
+
+  // ---- the fragments of one whole step
+  const int fr = lane & 31;
+  const int fsw = (fr >> 1) & 7;
+  const int a_frow = (wm * WAVE_M + fr) * ROW;
+  const int b_frow = Cfg::TM * ROW + (wn * Cfg::WAVE_N + fr) * ROW;
+  const int kx = lane >> 5;
+  bf16x8 fa[4][MSUB], fb[4][Cfg::NSUB];
+
+  if (group == 0) {
+    dma_step(0);
+    wait_vmcnt<0>();
+  }
+  __syncthreads();                 // step 0 published
+  if (group == 1) __syncthreads(); // group 1 runs one phase behind
+
+  for (int kt = 0; kt < nk; ++kt) {
+    // memory phase
+    if (group == 0) dma_step(kt + 1);
+    const char* base = lds + (kt & 1) * Cfg::STAGE_BYTES;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int ko = (((2 * s) | kx) ^ fsw) << 4;
+#pragma unroll
+      for (int m = 0; m < MSUB; ++m) fa[s][m] = *reinterpret_cast<const bf16x8*>(base + a_frow + m * 32 * ROW + ko);
+#pragma unroll
+      for (int n = 0; n < Cfg::NSUB; ++n)
+        fb[s][n] = *reinterpret_cast<const bf16x8*>(base + b_frow + n * 32 * ROW + ko);
+    }
+    // keep the phases apart: the scheduler must not move MFMAs (not memory operations) across
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    // compute phase
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int m = 0; m < MSUB; ++m)
+#pragma unroll
+        for (int n = 0; n < Cfg::NSUB; ++n)
+          acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s][m], fb[s][n], acc[m][n], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (group == 0) wait_vmcnt<0>();  // this wavefront's loads of step kt+1 have landed
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (group == 0) __syncthreads(); // same barrier count for both groups
+  wait_vmcnt<0>();                 // trailing out-of-range loads still write LDS
+  __syncthreads();
+}
+
+// =============================================================================================
+// Main loop v6: ping-pong on a ring of NS stages of K = 32, loads shared by both groups.
+// =============================================================================================
+//
+// As v5, two groups of four wavefronts alternate between a memory phase and a compute phase, with
+// group 1 one phase behind.  Here a step is K = 32 (16 MFMAs per wavefront) and every wavefront
+// issues its own share of the global -> LDS loads of step k+2 in its memory phase of step k, so the
+// texture unit gets one quarter of a step's bytes per phase instead of a whole step at once.
+//
+//   iteration k, memory phase:  loads of step k+2 into stage (k+2) % NS (last read two steps ago);
+//                               fragments of step k from stage k % NS;
+//                               group 1 then waits for its loads of step k+1
+//   iteration k, compute phase: 16 MFMAs of step k; group 0 then waits for its loads of step k+1
+//
+// Each group's loads of step k+1 have landed before the barrier that precedes group 0's memory
+// phase of step k+1 (group 0 waits at the end of its compute phase, group 1 at the end of its memory
+// phase, one phase later in time), giving each load three to four phases of slack.
+
+template <class Cfg>
+__device__ __forceinline__ void tile_mainloop6(const __bf16* __restrict__ A, int64_t lda, int rowsA,
+                                               const __bf16* __restrict__ B, int64_t ldb, int rowsB, int K,
+                                               char* __restrict__ lds, f32x16 (&acc)[MSUB][Cfg::NSUB]) {
+  static_assert(Cfg::NWAVES == 8 && Cfg::NS >= 3 && Cfg::BK == 32, "v6: 8 wavefronts, K32 ring");
+  constexpr int ROW = Cfg::ROW;
+  constexpr int NS = Cfg::NS;
+  constexpr int NDMA = Cfg::A_IPW + Cfg::B_IPW;   // load instructions per wavefront per step
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int group = wave >> 2;
+  const int wm = wave % Cfg::WM;
+  const int wn = wave / Cfg::WM;
+
+  const u32x4 da = make_desc(A, (uint32_t)((int64_t)rowsA * lda * 2));
+  const u32x4 db = make_desc(B, (uint32_t)((int64_t)rowsB * ldb * 2));
+  const uint32_t lds0 = lds_addr(lds);
+  const int dl_row = lane / Cfg::CPR;
+  const int dl_pc = lane % Cfg::CPR;
+  uint32_t d_off[NDMA];
+  int d_lc[NDMA];
+#pragma unroll
+  for (int d = 0; d < NDMA; ++d) {
+    const bool is_a = d < Cfg::A_IPW;
+    const int i = is_a ? d : d - Cfg::A_IPW;
+    const int r = (wave * (is_a ? Cfg::A_IPW : Cfg::B_IPW) + i) * Cfg::RPI + dl_row;
+    d_lc[d] = dl_pc ^ Cfg::swz(r);
+    d_off[d] = (uint32_t)(r * (is_a ? lda : ldb) * 2 + d_lc[d] * 16);
+  }
+  const int nk = (K + Cfg::BK - 1) / Cfg::BK;
+  auto dma_step = [&](int kt) {
+    const uint32_t sbase = lds0 + (kt % NS) * Cfg::STAGE_BYTES;
+#pragma unroll
+    for (int d = 0; d < NDMA; ++d) {
+      const bool is_a = d < Cfg::A_IPW;
+      const int i = is_a ? d : d - Cfg::A_IPW;
+      const bool ok = kt < nk && kt * Cfg::BK + d_lc[d] * 8 < K;
+      const uint32_t dst = sbase + (is_a ? (wave * Cfg::A_IPW + i) * 1024 : Cfg::TM * ROW + (wave * Cfg::B_IPW + i) * 1024);
+      dma16(is_a ? da : db, ok ? d_off[d] + (uint32_t)kt * ROW : OOB_OFFSET, dst);
+    }
+  };
+
+  const int fr = lane & 31;
+  const int fsw = Cfg::swz(fr);
+  const int a_frow = (wm * WAVE_M + fr) * ROW;
+  const int b_frow = Cfg::TM * ROW + (wn * Cfg::WAVE_N + fr) * ROW;
+  const int kx = lane >> 5;
+  bf16x8 fa[2][MSUB], fb[2][Cfg::NSUB];
+
+  dma_step(0);
+  dma_step(1);
+  wait_vmcnt<NDMA>();              // this wavefront's loads of step 0
+  __syncthreads();                 // step 0 published
+  if (group == 1) __syncthreads(); // group 1 runs one phase behind
+
+  for (int kt = 0; kt < nk; ++kt) {
+    // memory phase
+    dma_step(kt + 2);
+    const char* base = lds + (kt % NS) * Cfg::STAGE_BYTES;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int ko = (((2 * s) | kx) ^ fsw) << 4;
+#pragma unroll
+      for (int m = 0; m < MSUB; ++m) fa[s][m] = *reinterpret_cast<const bf16x8*>(base + a_frow + m * 32 * ROW + ko);
+#pragma unroll
+      for (int n = 0; n < Cfg::NSUB; ++n)
+        fb[s][n] = *reinterpret_cast<const bf16x8*>(base + b_frow + n * 32 * ROW + ko);
+    }
+    if (group == 1) wait_vmcnt<NDMA>();   // group 1's loads of step kt+1 have landed
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    // compute phase
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int m = 0; m < MSUB; ++m)
+#pragma unroll
+        for (int n = 0; n < Cfg::NSUB; ++n)
+          acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s][m], fb[s][n], acc[m][n], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (group == 0) wait_vmcnt<NDMA>();   // group 0's loads of step kt+1 have landed
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (group == 0) __syncthreads(); // same barrier count for both groups
+  wait_vmcnt<0>();                 // trailing out-of-range loads still write LDS
+  __syncthreads();
+}
+
+// =============================================================================================
+// Main loop v7: ping-pong on K = 64 steps with separate A and B rings (3 + 2 slots of 32 KB).
+// =============================================================================================
+//
+// As v5 (one K = 64 step per phase, full-step fragments in registers), but the global -> LDS loads
+// of a step are split between the groups so that neither group's memory phase carries a whole
+// step: group 1 loads the A rows (256 x 128 B) of step k+2 into A slot (k+2) % 3 during its memory
+// phase of step k, and group 0 loads the B rows of step k+1 into B slot (k+1) % 2 during its memory
+// phase of step k.  In phase terms (group 0 in even phases, group 1 one phase behind):
+//   A slot (k+2) % 3 was last read in phases 2k-2 and 2k-1, and is needed again in phase 2k+4;
+//   B slot (k+1) % 2 was last read in phases 2k-2 and 2k-1, and is needed again in phase 2k+2.
+// Group 1 waits for its A loads of step k+1 at the end of its memory phase of step k (phase 2k+1);
+// group 0 waits for its B loads of step k+1 at the end of its compute phase of step k (phase 2k+1).
+
+template <class Cfg>
+__device__ __forceinline__ void tile_mainloop7(const __bf16* __restrict__ A, int64_t lda, int rowsA,
+                                               const __bf16* __restrict__ B, int64_t ldb, int rowsB, int K,
+                                               char* __restrict__ lds, f32x16 (&acc)[MSUB][Cfg::NSUB]) {
+  static_assert(Cfg::NWAVES == 8 && Cfg::WM == 2 && Cfg::BK == 64 && Cfg::TM == 256 && Cfg::TN == 256,
+                "v7: 8 wavefronts, 256 x 256, K64");
+  constexpr int ROW = Cfg::ROW;                 // 128 bytes
+  constexpr int SLOT = 256 * ROW;               // 32 KB: one operand of one step
+  constexpr int B_BASE = 3 * SLOT;              // A slots 0..2, then B slots 0..1
+  constexpr int DPW = 8;                        // DMA instructions per wavefront per step (8 rows each)
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int group = wave >> 2;
+  const int gw = wave & 3;
+  const int wm = wave % Cfg::WM;
+  const int wn = wave / Cfg::WM;
+
+  // group 1 loads A, group 0 loads B; wavefront gw of a group loads rows [64 gw, 64 gw + 64)
+  const bool loads_a = group == 1;
+  const u32x4 desc = loads_a ? make_desc(A, (uint32_t)((int64_t)rowsA * lda * 2))
+                             : make_desc(B, (uint32_t)((int64_t)rowsB * ldb * 2));
+  const int64_t ld = loads_a ? lda : ldb;
+  const uint32_t lds0 = lds_addr(lds);
+  const int dl_row = lane >> 3;
+  const int dl_pc = lane & 7;
+  const int blk0 = gw * DPW;                    // even
+  const int lc_even = dl_pc ^ (dl_row >> 1);
+  const int lc_odd = dl_pc ^ (4 + (dl_row >> 1));
+  const uint32_t row_off = (uint32_t)((blk0 * 8 + dl_row) * ld * 2);
+  const uint32_t blk_stride = (uint32_t)(8 * ld * 2);
+  const int nk = (K + Cfg::BK - 1) / Cfg::BK;
+  auto dma_step = [&](int kt) {   // this group's operand of step kt into its slot
+    const bool kt_in = kt < nk;
+    const int k0 = kt * Cfg::BK;
+    const bool ok_even = kt_in && k0 + lc_even * 8 < K;
+    const bool ok_odd = kt_in && k0 + lc_odd * 8 < K;
+    const uint32_t ve = row_off + lc_even * 16 + (uint32_t)kt * ROW;
+    const uint32_t vo = row_off + lc_odd * 16 + (uint32_t)kt * ROW;
+    const uint32_t sbase = lds0 + (loads_a ? (kt % 3) * SLOT : B_BASE + (kt & 1) * SLOT) + blk0 * 1024;
+#pragma unroll
+    for (int i = 0; i < DPW; ++i) {
+      const bool ok = (i & 1) ? ok_odd : ok_even;
+      const uint32_t voff = ((i & 1) ? vo : ve) + (uint32_t)i * blk_stride;
+      dma16(desc, ok ? voff : OOB_OFFSET, sbase + i * 1024);
+    }
+  };
+
+  const int fr = lane & 31;
+  const int fsw = (fr >> 1) & 7;
+  const int a_frow = (wm * WAVE_M + fr) * ROW;
+  const int b_frow = (wn * Cfg::WAVE_N + fr) * ROW;
+  const int kx = lane >> 5;
+  bf16x8 fa[4][MSUB], fb[4][Cfg::NSUB];
+
+  // prologue: A of steps 0 and 1 (group 1), B of step 0 (group 0); step 0 published
+  dma_step(0);
+  if (loads_a) {
+    dma_step(1);
+    wait_vmcnt<DPW>();
+  } else {
+    wait_vmcnt<0>();
+  }
+  __syncthreads();
+  if (group == 1) __syncthreads();  // group 1 runs one phase behind
+
+  for (int kt = 0; kt < nk; ++kt) {
+    // memory phase
+    dma_step(loads_a ? kt + 2 : kt + 1);
+    const char* abase = lds + (kt % 3) * SLOT;
+    const char* bbase = lds + B_BASE + (kt & 1) * SLOT;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int ko = (((2 * s) | kx) ^ fsw) << 4;
+#pragma unroll
+      for (int m = 0; m < MSUB; ++m) fa[s][m] = *reinterpret_cast<const bf16x8*>(abase + a_frow + m * 32 * ROW + ko);
+#pragma unroll
+      for (int n = 0; n < Cfg::NSUB; ++n)
+        fb[s][n] = *reinterpret_cast<const bf16x8*>(bbase + b_frow + n * 32 * ROW + ko);
+    }
+    if (loads_a) wait_vmcnt<DPW>();   // group 1's A of step kt+1 has landed
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    // compute phase
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int m = 0; m < MSUB; ++m)
+#pragma unroll
+        for (int n = 0; n < Cfg::NSUB; ++n)
+          acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s][m], fb[s][n], acc[m][n], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (!loads_a) wait_vmcnt<0>();    // group 0's B of step kt+1 has landed
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (group == 0) __syncthreads();    // same barrier count for both groups
+  wait_vmcnt<0>();                    // trailing out-of-range loads still write LDS
+  __syncthreads();
+}
+
 }  // namespace lmh
