@@ -38,46 +38,45 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void bwd_dz_kernel(
   tile_coords<8>(blockIdx.x, gridDim.x, n_mt, n_nt, mt, nt);
   const int v0 = mt * Cfg::TM;  // local vocabulary row inside the step
   const int t0 = nt * Cfg::TN;
-  f32x16 acc[MSUB][Cfg::NSUB];
+  f32x4 acc[MSUB][Cfg::NSUB];
 #pragma unroll
   for (int m = 0; m < MSUB; ++m)
 #pragma unroll
-    for (int n = 0; n < Cfg::NSUB; ++n) acc[m][n] = (f32x16)(0.0f);
-  tile_mainloop3<Cfg>(weight + (int64_t)(vs0 + v0) * H, H, min(Cfg::TM, Vc - v0), hidden + (int64_t)t0 * H, H,
-                      min(Cfg::TN, T - t0), H, lds, acc);
+    for (int n = 0; n < Cfg::NSUB; ++n) acc[m][n] = (f32x4)(0.0f);
+  tile_mainloop_pipelined<Cfg>(weight + (int64_t)(vs0 + v0) * H, H, min(Cfg::TM, Vc - v0), hidden + (int64_t)t0 * H,
+                               H, min(Cfg::TN, T - t0), H, lds, acc);
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave % Cfg::WM, wn = wave / Cfg::WM;
-  const int j = lane & 31;
-  const int hf = lane >> 5;
+  const int j = acc_col(lane);
+  const int g4 = lane >> 4;
   const int wv = v0 + wm * WAVE_M;             // local column of this wavefront's first entry
   const int tok0 = t0 + wn * Cfg::WAVE_N;
   char* wl = lds + wave * Cfg::WAVE_N * DZ_PITCH;
 
+  // dz of the lane's four consecutive entries 16 m + 4 g4 + (0..3) of token n * 16 + j, staged
+  // token-major in LDS
 #pragma unroll
   for (int n = 0; n < Cfg::NSUB; ++n) {
-    const int tok = tok0 + n * 32 + j;
+    const int tok = tok0 + n * MFMA_MN + j;
     const bool tok_ok = tok < T;
     const float g = tok_ok ? grad[tok] : 0.f;
     const float L = tok_ok ? lse[tok] : 0.f;
     const int y = tok_ok ? labels[tok] : -1;
 #pragma unroll
-    for (int m = 0; m < MSUB; ++m)
+    for (int m = 0; m < MSUB; ++m) {
+      bf16x4 pk;
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        bf16x4 pk;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = m * 32 + 8 * g4 + 4 * hf + q;
-          const int v = vs0 + wv + col;
-          const float p = __builtin_amdgcn_exp2f((acc[m][n][4 * g4 + q] - L) * LOG2E);
-          const float oh = v == y ? 1.f : 0.f;
-          const float d = v < V ? g * (oh - p) : 0.f;
-          pk[q] = (__bf16)d;
-        }
-        *reinterpret_cast<bf16x4*>(wl + (n * 32 + j) * DZ_PITCH + (m * 32 + 8 * g4 + 4 * hf) * 2) = pk;
+      for (int i = 0; i < 4; ++i) {
+        const int v = vs0 + wv + m * MFMA_MN + acc_row(i, lane);
+        const float p = __builtin_amdgcn_exp2f((acc[m][n][i] - L) * LOG2E);
+        const float oh = v == y ? 1.f : 0.f;
+        const float d = v < V ? g * (oh - p) : 0.f;
+        pk[i] = (__bf16)d;
       }
+      *reinterpret_cast<bf16x4*>(wl + (n * MFMA_MN + j) * DZ_PITCH + (m * MFMA_MN + 4 * g4) * 2) = pk;
+    }
   }
   __syncthreads();
   // copy the wavefront's [WAVE_N tokens x 128 entries] block out, 16 bytes per lane
@@ -170,33 +169,33 @@ __device__ __forceinline__ void gemm_tn_tile(const GemmProblem& p, int bid, int 
   const int wave = threadIdx.x >> 6;
   const int wm = wave % Cfg::WM, wn = wave / Cfg::WM;
   const int rbase = m0 + wm * WAVE_M;
-  const int cbase = n0 + wn * Cfg::WAVE_N + (lane & 31);
+  const int cbase = n0 + wn * Cfg::WAVE_N + acc_col(lane);
 
   // the accumulator starts at C when accumulating, so the MFMA chain continues across calls
-  f32x16 acc[MSUB][Cfg::NSUB];
+  f32x4 acc[MSUB][Cfg::NSUB];
 #pragma unroll
   for (int m = 0; m < MSUB; ++m)
 #pragma unroll
     for (int n = 0; n < Cfg::NSUB; ++n)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = rbase + m * 32 + acc_row(r, lane);
-        const int col = cbase + n * 32;
-        acc[m][n][r] = (p.accumulate && row < p.M && col < p.N) ? p.C[(int64_t)row * p.ldc + col] : 0.f;
+      for (int i = 0; i < 4; ++i) {
+        const int row = rbase + m * MFMA_MN + acc_row(i, lane);
+        const int col = cbase + n * MFMA_MN;
+        acc[m][n][i] = (p.accumulate && row < p.M && col < p.N) ? p.C[(int64_t)row * p.ldc + col] : 0.f;
       }
 
-  tile_mainloop3<Cfg>(p.A + (int64_t)m0 * p.lda, p.lda, min(Cfg::TM, p.M - m0), p.B + (int64_t)n0 * p.ldb, p.ldb,
-                      min(Cfg::TN, p.N - n0), p.K, lds, acc);
+  tile_mainloop_pipelined<Cfg>(p.A + (int64_t)m0 * p.lda, p.lda, min(Cfg::TM, p.M - m0), p.B + (int64_t)n0 * p.ldb,
+                               p.ldb, min(Cfg::TN, p.N - n0), p.K, lds, acc);
 
 #pragma unroll
   for (int m = 0; m < MSUB; ++m)
 #pragma unroll
     for (int n = 0; n < Cfg::NSUB; ++n)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = rbase + m * 32 + acc_row(r, lane);
-        const int col = cbase + n * 32;
-        if (row < p.M && col < p.N) p.C[(int64_t)row * p.ldc + col] = acc[m][n][r];
+      for (int i = 0; i < 4; ++i) {
+        const int row = rbase + m * MFMA_MN + acc_row(i, lane);
+        const int col = cbase + n * MFMA_MN;
+        if (row < p.M && col < p.N) p.C[(int64_t)row * p.ldc + col] = acc[m][n][i];
       }
 }
 
@@ -258,9 +257,9 @@ BwdLayout bwd_layout(int64_t T, int64_t H, int64_t V) {
   return L;
 }
 
-// 256 x 256 tiles, 8 wavefronts (2 per SIMD), two LDS stages of K = 64, main loop 3
-using CfgDz = PipeCfg<2, 4, 2, 2, 64>;
-using CfgGrad = PipeCfg<2, 4, 2, 2, 64>;
+// 256 x 256 tiles, 8 wavefronts (2 per SIMD), two LDS stages of K = 64, pipelined main loop
+using CfgDz = PipeCfg<2, 4, 4, 2, 64>;
+using CfgGrad = PipeCfg<2, 4, 4, 2, 64>;
 
 void launch_bwd(const BwdArgs& a, hipStream_t stream) {
   const BwdLayout& L = a.L;

@@ -1,7 +1,7 @@
 // fwd.hip — forward kernels of the fused LM-head log-prob.
 //
 // K1 fwd_partials: the logit tile z = W_tile . h_tile^T (vocabulary on the MFMA M axis, tokens on
-//    the N axis, so each lane holds 64 vocabulary entries of one token and the per-token softmax
+//    the N axis, so each lane holds 32 vocabulary entries of one token and the per-token softmax
 //    reduction is mostly in-lane).  Its epilogue reduces every (token, 128-entry vocabulary
 //    chunk) to one record {m, n, b, u}:
 //        m = max z,  n = #{z == m},  b = sum_{z < m} exp(z - m),  u = sum exp(z - m) (z - m)
@@ -17,53 +17,24 @@
 //    out-of-vocabulary label.)
 #include "kernels.hpp"
 
-// Build-time tuning knobs for the large-T tile (all choices give the same bits: the per-wavefront
-// vocabulary extent and the MFMA chain are fixed).
-#ifndef LMH_BIG_WN
-#define LMH_BIG_WN 4
-#endif
-#ifndef LMH_BIG_NSUB
-#define LMH_BIG_NSUB 2
-#endif
-#ifndef LMH_BIG_NS
-#define LMH_BIG_NS 2
-#endif
-#ifndef LMH_BIG_BK
-#define LMH_BIG_BK 64
-#endif
+// Build-time tuning knobs (all choices give the same bits: the per-wavefront vocabulary extent
+// and the MFMA chain are fixed).
+// large-T tile: 256 x 256, 8 wavefronts, ping-pong main loop; XCD tile grouping
 #ifndef LMH_GROUP_M
 #define LMH_GROUP_M 8
 #endif
-// small-T tile (T <= 32): wavefronts along the vocabulary, stages, K step, main loop
-#ifndef LMH_SMALL_WM
-#define LMH_SMALL_WM 2
-#endif
+// small-T tiles (T <= 32 and 32 < T <= 64): stages and K step of the spread main loop
 #ifndef LMH_SMALL_NS
 #define LMH_SMALL_NS 4
 #endif
 #ifndef LMH_SMALL_BK
 #define LMH_SMALL_BK 64
 #endif
-#ifndef LMH_SMALL_LOOP
-#define LMH_SMALL_LOOP 4
-#endif
-// 32 < T <= 64 tile
-#ifndef LMH_S64_WM
-#define LMH_S64_WM 2
-#endif
 #ifndef LMH_S64_NS
 #define LMH_S64_NS 4
 #endif
 #ifndef LMH_S64_BK
 #define LMH_S64_BK 64
-#endif
-#ifndef LMH_S64_LOOP
-#define LMH_S64_LOOP 4
-#endif
-// main loop of the large tile: 3 = software-pipelined fragments (tile_mainloop3), 4 = ring with
-// the loads spread between MFMAs (tile_mainloop4, >= 3 stages), 2 = plain ring (tile_mainloop2)
-#ifndef LMH_BIG_LOOP
-#define LMH_BIG_LOOP 7
 #endif
 
 namespace lmh {
@@ -77,68 +48,74 @@ namespace lmh {
 // it adds exactly zero to every sum (0 * d is -0 for finite d).
 constexpr float MASKED_LOGIT = -1.0e30f;
 
+// Lane l holds, for each of its NSUB tokens (column l % 16 of an MFMA block), the 32 entries at
+// wavefront rows 16 m + 4 (l / 16) + i; lanes l, l^16, l^32, l^48 together hold the token's 128.
 template <int NSUB, bool TAIL>
-__device__ __forceinline__ void fwd_records(f32x16 (&acc)[MSUB][NSUB], int lane, int wave_v0, int tok0, int T,
+__device__ __forceinline__ void fwd_records(f32x4 (&acc)[MSUB][NSUB], int lane, int wave_v0, int tok0, int T,
                                             int V, const int* __restrict__ labels, f32x4* __restrict__ rec,
                                             float* __restrict__ zy, int chunk) {
-  const int j = lane & 31;
-  const int hf = lane >> 5;
+  const int j = acc_col(lane);
+  const int g = lane >> 4;
   if (TAIL) {
 #pragma unroll
     for (int m = 0; m < MSUB; ++m)
 #pragma unroll
       for (int n = 0; n < NSUB; ++n)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (wave_v0 + m * 32 + acc_row(r, lane) >= V) acc[m][n][r] = MASKED_LOGIT;
+        for (int i = 0; i < 4; ++i)
+          if (wave_v0 + m * MFMA_MN + acc_row(i, lane) >= V) acc[m][n][i] = MASKED_LOGIT;
   }
 #pragma unroll
   for (int n = 0; n < NSUB; ++n) {
-    const int tok = tok0 + n * 32 + j;
+    const int tok = tok0 + n * MFMA_MN + j;
     const bool tok_ok = tok < T;
     const int y = tok_ok ? labels[tok] : -1;
 
-    // pass 1: chunk max over this lane's 64 entries, then across the lane pair (l, l^32), which
-    // together hold the wavefront's 128 entries of this token
+    // pass 1: chunk max over this lane's 32 entries, then across the four lanes of the token
     float mx = acc[0][n][0];
 #pragma unroll
     for (int m = 0; m < MSUB; ++m)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[m][n][r]);
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, acc[m][n][i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
 
-    // pass 2: count at the max, sum of exp below it, sum of exp * shift (fixed order: m, then r)
+    // pass 2: count at the max, sum of exp below it, sum of exp * shift (fixed order: m, then i)
     float cnt = 0.f, b = 0.f, u = 0.f;
 #pragma unroll
     for (int m = 0; m < MSUB; ++m)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float d = acc[m][n][r] - mx;
+      for (int i = 0; i < 4; ++i) {
+        const float d = acc[m][n][i] - mx;
         const float e = __builtin_amdgcn_exp2f(d * LOG2E);
         const bool at_max = d == 0.f;
         cnt += at_max ? 1.f : 0.f;
         b += at_max ? 0.f : e;
         u = __builtin_fmaf(e, d, u);
       }
-    // the pair's partial sums: a + b == b + a, so both lanes hold the same bits
+    // the four lanes' partial sums as (s0 + s1) + (s2 + s3): by commutativity of each addition,
+    // every lane of the token ends with the same bits
+    cnt += __shfl_xor(cnt, 16);
+    b += __shfl_xor(b, 16);
+    u += __shfl_xor(u, 16);
     cnt += __shfl_xor(cnt, 32);
     b += __shfl_xor(b, 32);
     u += __shfl_xor(u, 32);
 
-    // label logit: local index w = y - wave_v0 sits in sub-tile w/32, lane half (w/4)%2,
-    // register 4*((w%32)/8) + w%4
+    // label logit: local index w = y - wave_v0 sits in block w / 16, lane group (w % 16) / 4,
+    // register w % 4
     const int w = y - wave_v0;
-    const bool mine = tok_ok && y < V && (unsigned)w < (unsigned)WAVE_M && ((w >> 2) & 1) == hf;
+    const bool mine = tok_ok && y < V && (unsigned)w < (unsigned)WAVE_M && ((w >> 2) & 3) == g;
     if (__any(mine)) {
-      const int idx = ((w >> 5) << 4) | (((w & 31) >> 3) << 2) | (w & 3);
+      const int idx = ((w >> 4) << 2) | (w & 3);
       float val = 0.f;
 #pragma unroll
       for (int m = 0; m < MSUB; ++m)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) val = (idx == m * 16 + r) ? acc[m][n][r] : val;
+        for (int i = 0; i < 4; ++i) val = (idx == m * 4 + i) ? acc[m][n][i] : val;
       if (mine) zy[tok] = val;
     }
-    if (hf == 0 && tok_ok) {
+    if (g == 0 && tok_ok) {
       f32x4 v;
       v[0] = mx;
       v[1] = cnt;
@@ -158,26 +135,20 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void fwd_partials_kernel(
   tile_coords<LMH_GROUP_M>(blockIdx.x, gridDim.x, n_mt, n_nt, mt, nt);
   const int v0 = mt * Cfg::TM;
   const int t0 = nt * Cfg::TN;
-  f32x16 acc[MSUB][Cfg::NSUB];
+  f32x4 acc[MSUB][Cfg::NSUB];
 #pragma unroll
   for (int m = 0; m < MSUB; ++m)
 #pragma unroll
-    for (int n = 0; n < Cfg::NSUB; ++n) acc[m][n] = (f32x16)(0.0f);
+    for (int n = 0; n < Cfg::NSUB; ++n) acc[m][n] = (f32x4)(0.0f);
   const __bf16* A = weight + (int64_t)v0 * H;
   const __bf16* B = hidden + (int64_t)t0 * H;
   const int rowsA = min(Cfg::TM, V - v0), rowsB = min(Cfg::TN, T - t0);
-  if constexpr (Cfg::LOOP == 7)
-    tile_mainloop7<Cfg>(A, H, rowsA, B, H, rowsB, H, lds, acc);
-  else if constexpr (Cfg::LOOP == 6)
-    tile_mainloop6<Cfg>(A, H, rowsA, B, H, rowsB, H, lds, acc);
-  else if constexpr (Cfg::LOOP == 5)
-    tile_mainloop5<Cfg>(A, H, rowsA, B, H, rowsB, H, lds, acc);
-  else if constexpr (Cfg::LOOP == 4)
-    tile_mainloop4<Cfg>(A, H, rowsA, B, H, rowsB, H, lds, acc);
-  else if constexpr (Cfg::LOOP == 3)
-    tile_mainloop3<Cfg>(A, H, rowsA, B, H, rowsB, H, lds, acc);
+  if constexpr (Cfg::LOOP == LOOP_PINGPONG)
+    tile_mainloop_pingpong<Cfg>(A, H, rowsA, B, H, rowsB, H, lds, acc);
+  else if constexpr (Cfg::LOOP == LOOP_SPREAD)
+    tile_mainloop_spread<Cfg>(A, H, rowsA, B, H, rowsB, H, lds, acc);
   else
-    tile_mainloop2<Cfg>(A, H, rowsA, B, H, rowsB, H, lds, acc);
+    tile_mainloop_pipelined<Cfg>(A, H, rowsA, B, H, rowsB, H, lds, acc);
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -304,20 +275,20 @@ static void launch_partials_cfg(const FwdArgs& a, hipStream_t stream) {
 template <class P, int LOOP_>
 struct FwdCfg : P {
   static constexpr int LOOP = LOOP_;
-  // the v7 loop keeps three A slots and two B slots of one K step each
-  static constexpr int LDS_BYTES = LOOP_ == 7 ? 5 * 256 * P::ROW : P::LDS_BYTES;
+  // the ping-pong loop keeps three A slots and two B slots of one K step each
+  static constexpr int LDS_BYTES = LOOP_ == LOOP_PINGPONG ? 5 * 256 * P::ROW : P::LDS_BYTES;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
-// 256 vocab x 256 tokens, 8 wavefronts (2 per SIMD) in two groups that alternate between loads and
-// MFMAs, K = 64 steps, three A slots and two B slots (160 KB of LDS)
-using CfgBig = FwdCfg<PipeCfg<2, LMH_BIG_WN, LMH_BIG_NSUB, LMH_BIG_NS, LMH_BIG_BK>, LMH_BIG_LOOP>;
-// 256 vocab x 128 tokens, 4 wavefronts, three stages of K = 64
-using CfgMid = FwdCfg<PipeCfg<2, 2, 2, 3, 64>, 3>;
+// T > 1024: 256 vocab x 256 tokens, 8 wavefronts (2 per SIMD) in two groups that alternate between
+// loads and MFMAs, K = 64 steps, three A slots and two B slots (160 KB of LDS)
+using CfgBig = FwdCfg<PipeCfg<2, 4, 4, 2, 64>, LOOP_PINGPONG>;
+// 64 < T <= 1024: 256 vocab x 128 tokens, 4 wavefronts, three stages of K = 64
+using CfgMid = FwdCfg<PipeCfg<2, 2, 4, 3, 64>, LOOP_PIPELINED>;
 // T <= 32: 256 vocab x 32 tokens, 2 wavefronts, four stages of K = 64 with the loads spread between
 // the MFMAs: the weight stream is HBM-bound here, so deep prefetch matters most
-using CfgSmall = FwdCfg<PipeCfg<LMH_SMALL_WM, 1, 1, LMH_SMALL_NS, LMH_SMALL_BK>, LMH_SMALL_LOOP>;
+using CfgSmall = FwdCfg<PipeCfg<2, 1, 2, LMH_SMALL_NS, LMH_SMALL_BK>, LOOP_SPREAD>;
 // 32 < T <= 64: 256 vocab x 64 tokens, 2 wavefronts, four stages of K = 64 (160 KB of LDS)
-using CfgS64 = FwdCfg<PipeCfg<LMH_S64_WM, 1, 2, LMH_S64_NS, LMH_S64_BK>, LMH_S64_LOOP>;
+using CfgS64 = FwdCfg<PipeCfg<2, 1, 4, LMH_S64_NS, LMH_S64_BK>, LOOP_SPREAD>;
 
 void launch_fwd_partials(const FwdArgs& a, hipStream_t stream) {
   if (a.T <= 32)
