@@ -25,7 +25,9 @@
  * the batch, or how the caller splits the rows into calls.  The per-row arithmetic is one fixed
  * sequence: one MFMA instruction shape and one K order over H, a per-row reduction inside a
  * fixed 128-column vocabulary chunk, and a fold of the chunk records in an order that depends on
- * V only.  There are no atomics and no T-dependent split of H or V.  (Megatron-LM PR #5897
+ * V only.  No value is combined by atomics and nothing splits H or V by T; the only atomic
+ * operations are the large-T forward's tile counters, which choose the workgroup that computes a
+ * tile, never what it computes.  (Megatron-LM PR #5897
  * "Batch-invariant train/inference logprob parity", commit message: a row's output must not
  * change with the total row count.)
  *
@@ -71,8 +73,9 @@ typedef enum {
 } lmh_status_t;
 
 /* Bytes of workspace lmhead_logprob_fwd needs (also the stage entry points below).  Returns 0 for
- * invalid sizes.  The workspace holds one 16-byte record per (row, 128-column vocabulary chunk)
- * plus one float per row. */
+ * invalid sizes.  The workspace holds one 16-byte record per (row, 128-column vocabulary chunk),
+ * one float per row and 256 bytes of tile-scheduler counters; its initial contents do not matter.
+ * Calls that may run concurrently need separate workspaces. */
 LMH_API size_t lmhead_logprob_fwd_workspace_size(int64_t T, int64_t H, int64_t V);
 
 /* Forward.  logprob is required; entropy and lse may be NULL (not computed / not written).

@@ -28,7 +28,7 @@ lmh_status_t check_sizes(int64_t T, int64_t H, int64_t V) {
 }
 
 struct FwdWs {
-  size_t rec_off, zy_off, total;
+  size_t rec_off, zy_off, sched_off, total;
 };
 
 FwdWs fwd_ws(int64_t T, int64_t V) {
@@ -36,7 +36,8 @@ FwdWs fwd_ws(int64_t T, int64_t V) {
   FwdWs w;
   w.rec_off = 0;
   w.zy_off = align256((size_t)n_c * (size_t)T * 16);
-  w.total = w.zy_off + align256((size_t)T * 4);
+  w.sched_off = w.zy_off + align256((size_t)T * 4);
+  w.total = w.sched_off + align256(lmh::SCHED_WORDS * sizeof(int));
   return w;
 }
 
@@ -60,6 +61,15 @@ lmh_status_t check_out(const float* p, bool required) {
 
 lmh_status_t launched() { return hipGetLastError() == hipSuccess ? LMH_OK : LMH_ERR_HIP; }
 
+// Compute units of the current device (the large-T forward grid has one workgroup per CU).
+lmh_status_t device_cus(int& cus) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return LMH_ERR_HIP;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return LMH_ERR_HIP;
+  if (cus < 8) cus = 8;
+  return LMH_OK;
+}
+
 FwdArgs make_fwd_args(const void* hidden, const void* weight, const int32_t* labels, int64_t T, int64_t H,
                       int64_t V, float* logprob, float* entropy, float* lse, void* workspace) {
   const FwdWs w = fwd_ws(T, V);
@@ -73,9 +83,11 @@ FwdArgs make_fwd_args(const void* hidden, const void* weight, const int32_t* lab
   a.V = (int)V;
   a.rec = reinterpret_cast<lmh::f32x4*>(ws + w.rec_off);
   a.zy = reinterpret_cast<float*>(ws + w.zy_off);
+  a.sched = reinterpret_cast<int*>(ws + w.sched_off);
   a.logprob = logprob;
   a.entropy = entropy;
   a.lse = lse;
+  a.cus = 0;
   return a;
 }
 
@@ -101,9 +113,10 @@ lmh_status_t lmhead_logprob_fwd_partials(const void* hidden, const void* weight,
   if (T == 0) return LMH_OK;
   LMH_TRY(check_inputs(hidden, weight, labels));
   LMH_TRY(check_ws(workspace, workspace_bytes, fwd_ws(T, V).total));
+  FwdArgs a = make_fwd_args(hidden, weight, labels, T, H, V, nullptr, nullptr, nullptr, workspace);
+  LMH_TRY(device_cus(a.cus));
   (void)hipGetLastError();  // clear any stale error so the check after launching sees only ours
-  lmh::launch_fwd_partials(make_fwd_args(hidden, weight, labels, T, H, V, nullptr, nullptr, nullptr, workspace),
-                           stream);
+  lmh::launch_fwd_partials(a, stream);
   return launched();
 }
 
@@ -134,8 +147,9 @@ lmh_status_t lmhead_logprob_fwd(const void* hidden, const void* weight, const in
   LMH_TRY(check_out(entropy, false));
   LMH_TRY(check_out(lse, false));
   LMH_TRY(check_ws(workspace, workspace_bytes, fwd_ws(T, V).total));
+  FwdArgs a = make_fwd_args(hidden, weight, labels, T, H, V, logprob, entropy, lse, workspace);
+  LMH_TRY(device_cus(a.cus));
   (void)hipGetLastError();
-  const FwdArgs a = make_fwd_args(hidden, weight, labels, T, H, V, logprob, entropy, lse, workspace);
   lmh::launch_fwd_partials(a, stream);
   if (hipGetLastError() != hipSuccess) return LMH_ERR_HIP;
   lmh::launch_fwd_finalize(a, stream);

@@ -50,9 +50,11 @@ constexpr float MASKED_LOGIT = -1.0e30f;
 
 // Lane l holds, for each of its NSUB tokens (column l % 16 of an MFMA block), the 32 entries at
 // wavefront rows 16 m + 4 (l / 16) + i; lanes l, l^16, l^32, l^48 together hold the token's 128.
+// lw[n] is the label's offset from wave_v0 for token n * 16 + l % 16 (any value outside [0, 128)
+// when the label is not in this chunk, out of vocabulary, or the token is past T).
 template <int NSUB, bool TAIL>
 __device__ __forceinline__ void fwd_records(f32x4 (&acc)[MSUB][NSUB], int lane, int wave_v0, int tok0, int T,
-                                            int V, const int* __restrict__ labels, f32x4* __restrict__ rec,
+                                            int V, const int (&lw)[NSUB], f32x4* __restrict__ rec,
                                             float* __restrict__ zy, int chunk) {
   const int j = acc_col(lane);
   const int g = lane >> 4;
@@ -69,7 +71,6 @@ __device__ __forceinline__ void fwd_records(f32x4 (&acc)[MSUB][NSUB], int lane, 
   for (int n = 0; n < NSUB; ++n) {
     const int tok = tok0 + n * MFMA_MN + j;
     const bool tok_ok = tok < T;
-    const int y = tok_ok ? labels[tok] : -1;
 
     // pass 1: chunk max over this lane's 32 entries, then across the four lanes of the token
     float mx = acc[0][n][0];
@@ -81,7 +82,8 @@ __device__ __forceinline__ void fwd_records(f32x4 (&acc)[MSUB][NSUB], int lane, 
     mx = fmaxf(mx, __shfl_xor(mx, 32));
 
     // pass 2: count at the max, sum of exp below it, sum of exp * shift (fixed order: m, then i)
-    float cnt = 0.f, b = 0.f, u = 0.f;
+    int cnt = 0;
+    float b = 0.f, u = 0.f;
 #pragma unroll
     for (int m = 0; m < MSUB; ++m)
 #pragma unroll
@@ -89,7 +91,7 @@ __device__ __forceinline__ void fwd_records(f32x4 (&acc)[MSUB][NSUB], int lane, 
         const float d = acc[m][n][i] - mx;
         const float e = __builtin_amdgcn_exp2f(d * LOG2E);
         const bool at_max = d == 0.f;
-        cnt += at_max ? 1.f : 0.f;
+        cnt += at_max;
         b += at_max ? 0.f : e;
         u = __builtin_fmaf(e, d, u);
       }
@@ -102,11 +104,11 @@ __device__ __forceinline__ void fwd_records(f32x4 (&acc)[MSUB][NSUB], int lane, 
     b += __shfl_xor(b, 32);
     u += __shfl_xor(u, 32);
 
-    // label logit: local index w = y - wave_v0 sits in block w / 16, lane group (w % 16) / 4,
-    // register w % 4
-    const int w = y - wave_v0;
-    const bool mine = tok_ok && y < V && (unsigned)w < (unsigned)WAVE_M && ((w >> 2) & 3) == g;
-    if (__any(mine)) {
+    // label logit: local index w sits in block w / 16, lane group (w % 16) / 4, register w % 4.
+    // Few chunks hold a label, so the select runs behind a wavefront-uniform branch.
+    const int w = lw[n];
+    const bool mine = (unsigned)w < (unsigned)WAVE_M && ((w >> 2) & 3) == g;
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(mine) != 0, 0)) {
       const int idx = ((w >> 4) << 2) | (w & 3);
       float val = 0.f;
 #pragma unroll
@@ -118,12 +120,46 @@ __device__ __forceinline__ void fwd_records(f32x4 (&acc)[MSUB][NSUB], int lane, 
     if (g == 0 && tok_ok) {
       f32x4 v;
       v[0] = mx;
-      v[1] = cnt;
+      v[1] = (float)cnt;
       v[2] = b;
       v[3] = u;
       rec[(size_t)chunk * (size_t)T + tok] = v;
     }
   }
+}
+
+// The wavefront's labels as offsets from its first vocabulary row (see fwd_records).
+template <int NSUB>
+__device__ __forceinline__ void label_offsets(const int (&y)[NSUB], int wave_v0, int V, int (&lw)[NSUB]) {
+#pragma unroll
+  for (int n = 0; n < NSUB; ++n) lw[n] = (y[n] >= 0 && y[n] < V) ? y[n] - wave_v0 : -1;
+}
+
+template <int NSUB>
+__device__ __forceinline__ void load_labels(const int* __restrict__ labels, int tok0, int lane, int T, int (&y)[NSUB]) {
+#pragma unroll
+  for (int n = 0; n < NSUB; ++n) {
+    const int tok = tok0 + n * MFMA_MN + acc_col(lane);
+    y[n] = tok < T ? labels[tok] : -1;
+  }
+}
+
+// Records of the wavefront's chunk of the tile at (v0, t0); lw from label_offsets.
+template <class Cfg>
+__device__ __forceinline__ void tile_records(f32x4 (&acc)[MSUB][Cfg::NSUB], int v0, int t0, int T, int V,
+                                             const int (&lw)[Cfg::NSUB], f32x4* __restrict__ rec,
+                                             float* __restrict__ zy) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave % Cfg::WM, wn = wave / Cfg::WM;
+  const int wave_v0 = v0 + wm * WAVE_M;
+  if (wave_v0 >= V) return;  // this wavefront's chunk lies wholly past the vocabulary
+  const int tok0 = t0 + wn * Cfg::WAVE_N;
+  const int chunk = wave_v0 / WAVE_M;
+  if (wave_v0 + WAVE_M <= V)
+    fwd_records<Cfg::NSUB, false>(acc, lane, wave_v0, tok0, T, V, lw, rec, zy, chunk);
+  else
+    fwd_records<Cfg::NSUB, true>(acc, lane, wave_v0, tok0, T, V, lw, rec, zy, chunk);
 }
 
 template <class Cfg>
@@ -143,24 +179,109 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void fwd_partials_kernel(
   const __bf16* A = weight + (int64_t)v0 * H;
   const __bf16* B = hidden + (int64_t)t0 * H;
   const int rowsA = min(Cfg::TM, V - v0), rowsB = min(Cfg::TN, T - t0);
-  if constexpr (Cfg::LOOP == LOOP_PINGPONG)
-    tile_mainloop_pingpong<Cfg>(A, H, rowsA, B, H, rowsB, H, lds, acc);
-  else if constexpr (Cfg::LOOP == LOOP_SPREAD)
+  if constexpr (Cfg::LOOP == LOOP_SPREAD)
     tile_mainloop_spread<Cfg>(A, H, rowsA, B, H, rowsB, H, lds, acc);
   else
     tile_mainloop_pipelined<Cfg>(A, H, rowsA, B, H, rowsB, H, lds, acc);
-
-  const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int wm = wave % Cfg::WM, wn = wave / Cfg::WM;
-  const int wave_v0 = v0 + wm * WAVE_M;
-  if (wave_v0 >= V) return;  // this wavefront's chunk lies wholly past the vocabulary
-  const int tok0 = t0 + wn * Cfg::WAVE_N;
-  const int chunk = wave_v0 / WAVE_M;
-  if (wave_v0 + WAVE_M <= V)
-    fwd_records<Cfg::NSUB, false>(acc, lane, wave_v0, tok0, T, V, labels, rec, zy, chunk);
-  else
-    fwd_records<Cfg::NSUB, true>(acc, lane, wave_v0, tok0, T, V, labels, rec, zy, chunk);
+  int y[Cfg::NSUB], lw[Cfg::NSUB];
+  load_labels(labels, t0 + (wave / Cfg::WM) * Cfg::WAVE_N, threadIdx.x & 63, T, y);
+  label_offsets(y, v0 + (wave % Cfg::WM) * WAVE_M, V, lw);
+  tile_records<Cfg>(acc, v0, t0, T, V, lw, rec, zy);
+}
+
+// Persistent form for the ping-pong tile: one workgroup per CU.
+//
+// Tiles are handed out by per-XCD counters in the workspace.  A workgroup on XCD x takes the next
+// tile of x's contiguous tile range (so the workgroups of an XCD work on neighbouring tiles
+// together, sharing A and B rows in that XCD's L2); once x's range is used up it takes tiles from
+// the other XCDs' ranges.  XCDs do not run at the same speed, and a static split leaves the fastest
+// idle at the end.  The counters decide only which workgroup computes a tile, never what it
+// computes: every tile's records are the same bits whoever computes them.
+//
+// The claim of the tile after next is issued during the current tile's epilogue and read after
+// the next tile's K loop, so its latency hides behind that loop.  The next tile's first loads are
+// issued before the finished tile's records are computed, so their latency hides behind that VALU
+// work, and no workgroup launch separates the tiles.
+
+// Thread 0: a tile from another XCD's range, or -1 when every range is used up.
+__device__ __noinline__ int steal_tile(int* sched, int xcd, int ntiles) {
+  for (int k = 1; k < 8; ++k) {
+    const int x = (xcd + k) & 7;
+    int start, count;
+    xcd_range(x, ntiles, start, count);
+    const int i = atomicAdd(&sched[x], 1);
+    if (i < count) return start + i;
+  }
+  return -1;
+}
+
+__global__ void fwd_sched_reset_kernel(int* __restrict__ sched) {
+  if (threadIdx.x < SCHED_WORDS) sched[threadIdx.x] = 0;
+}
+
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::NTHREADS) void fwd_partials_persistent_kernel(
+    const __bf16* __restrict__ hidden, const __bf16* __restrict__ weight, const int* __restrict__ labels,
+    int T, int H, int V, int n_mt, int n_nt, f32x4* __restrict__ rec, float* __restrict__ zy,
+    int* __restrict__ sched) {
+  __shared__ __attribute__((aligned(1024))) char lds[Cfg::LDS_BYTES];
+  // Tile numbers are passed from thread 0 to the workgroup through the first word of B slot 1,
+  // which no load writes between the end of one K loop and the first barrier of the next.
+  int* const bc = reinterpret_cast<int*>(lds + PingPong<Cfg>::B_BASE + PingPong<Cfg>::SLOT);
+  const int ntiles = n_mt * n_nt;
+  const int xcd = blockIdx.x & 7;
+  int xs, xc;
+  xcd_range(xcd, ntiles, xs, xc);
+  const int wm = (threadIdx.x >> 6) % Cfg::WM;
+  const int wn = (threadIdx.x >> 6) / Cfg::WM;
+  const int lane = threadIdx.x & 63;
+
+  auto own_or_steal = [&](int i) { return i < xc ? xs + i : steal_tile(sched, xcd, ntiles); };
+  if (threadIdx.x == 0) bc[0] = own_or_steal(atomicAdd(&sched[xcd], 1));
+  __syncthreads();
+  int L = bc[0];
+  if (L < 0) return;
+
+  PingPong<Cfg> pp(lds);
+  int mt, nt;
+  group_coords<LMH_GROUP_M>(L, n_mt, n_nt, mt, nt);
+  int v0 = mt * Cfg::TM, t0 = nt * Cfg::TN;
+  pp.start(weight + (int64_t)v0 * H, H, min(Cfg::TM, V - v0), hidden + (int64_t)t0 * H, H, min(Cfg::TN, T - t0), H);
+  int claim = 0;  // thread 0: raw counter value of the next claim on this XCD's range
+  if (threadIdx.x == 0) claim = atomicAdd(&sched[xcd], 1);
+  for (;;) {
+    int y[Cfg::NSUB];
+    load_labels(labels, t0 + wn * Cfg::WAVE_N, lane, T, y);
+    f32x4 acc[MSUB][Cfg::NSUB];
+#pragma unroll
+    for (int m = 0; m < MSUB; ++m)
+#pragma unroll
+      for (int n = 0; n < Cfg::NSUB; ++n) acc[m][n] = (f32x4)(0.0f);
+    pp.run(acc);
+    // The labels are consumed here, before the next tile's loads go out: the compiler's wait for
+    // them then covers nothing else.
+    int lw[Cfg::NSUB];
+    label_offsets(y, v0 + wm * WAVE_M, V, lw);
+    if (threadIdx.x == 0) bc[0] = own_or_steal(claim);
+    __syncthreads();
+    const int Ln = bc[0];
+    __builtin_amdgcn_sched_barrier(0);
+    int v0n = 0, t0n = 0;
+    if (Ln >= 0) {
+      group_coords<LMH_GROUP_M>(Ln, n_mt, n_nt, mt, nt);
+      v0n = mt * Cfg::TM;
+      t0n = nt * Cfg::TN;
+      pp.start(weight + (int64_t)v0n * H, H, min(Cfg::TM, V - v0n), hidden + (int64_t)t0n * H, H,
+               min(Cfg::TN, T - t0n), H);
+      if (threadIdx.x == 0) claim = atomicAdd(&sched[xcd], 1);
+    }
+    tile_records<Cfg>(acc, v0, t0, T, V, lw, rec, zy);
+    if (Ln < 0) break;
+    L = Ln;
+    v0 = v0n;
+    t0 = t0n;
+  }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -266,8 +387,16 @@ template <class Cfg>
 static void launch_partials_cfg(const FwdArgs& a, hipStream_t stream) {
   const int n_mt = (a.V + Cfg::TM - 1) / Cfg::TM;
   const int n_nt = (a.T + Cfg::TN - 1) / Cfg::TN;
-  hipLaunchKernelGGL(fwd_partials_kernel<Cfg>, dim3(n_mt * n_nt), dim3(Cfg::NTHREADS), 0, stream, a.hidden,
-                     a.weight, a.labels, a.T, a.H, a.V, n_mt, n_nt, a.rec, a.zy);
+  if constexpr (Cfg::LOOP == LOOP_PINGPONG) {
+    // one workgroup per CU (the tile takes all of a CU's LDS)
+    const int ntiles = n_mt * n_nt;
+    hipLaunchKernelGGL(fwd_sched_reset_kernel, dim3(1), dim3(64), 0, stream, a.sched);
+    hipLaunchKernelGGL(fwd_partials_persistent_kernel<Cfg>, dim3(min(ntiles, a.cus)), dim3(Cfg::NTHREADS), 0,
+                       stream, a.hidden, a.weight, a.labels, a.T, a.H, a.V, n_mt, n_nt, a.rec, a.zy, a.sched);
+  } else {
+    hipLaunchKernelGGL(fwd_partials_kernel<Cfg>, dim3(n_mt * n_nt), dim3(Cfg::NTHREADS), 0, stream, a.hidden,
+                       a.weight, a.labels, a.T, a.H, a.V, n_mt, n_nt, a.rec, a.zy);
+  }
 }
 
 // Tile configurations, chosen by T.  Each has a 128-entry vocabulary extent per wavefront and the

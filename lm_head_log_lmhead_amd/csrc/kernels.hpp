@@ -16,6 +16,9 @@ constexpr int VOCAB_CHUNK = WAVE_M;
 // accumulation chain.
 constexpr int BWD_VOCAB_STEP = 16384;
 
+// Words of the forward workspace used by the large-T tile scheduler (one counter per XCD).
+constexpr int SCHED_WORDS = 16;
+
 struct FwdArgs {
   const __bf16* hidden;
   const __bf16* weight;
@@ -23,9 +26,11 @@ struct FwdArgs {
   int T, H, V;
   f32x4* rec;   // [n_c][T] records
   float* zy;    // [T] label logits
+  int* sched;   // [SCHED_WORDS] tile counters, reset by the partials launch
   float* logprob;
   float* entropy;
   float* lse;
+  int cus;      // compute units of the device (persistent grids)
 };
 
 void launch_fwd_partials(const FwdArgs& a, hipStream_t stream);

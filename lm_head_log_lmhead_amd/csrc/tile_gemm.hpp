@@ -48,16 +48,18 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// Workgroup id -> (m tile, n tile).  Consecutive workgroup ids are dealt round-robin to the 8
-// XCDs; the remap gives each XCD one contiguous range of logical tiles, and inside a range tiles
-// go in groups of GROUP_M m-tiles by all n-tiles, so the workgroups running together on one XCD
+// Workgroup tile order.  Consecutive workgroup ids are dealt round-robin to the 8 XCDs; xcd_range
+// gives each XCD one contiguous range of logical tiles, and inside a range tiles go in groups of
+// GROUP_M m-tiles by all n-tiles (group_coords), so the workgroups running together on one XCD
 // share both their A rows and their B rows in that XCD's L2.
+__device__ __forceinline__ void xcd_range(int xcd, int ntiles, int& start, int& count) {
+  const int q = ntiles >> 3, rem = ntiles & 7;
+  start = xcd < rem ? xcd * (q + 1) : rem * (q + 1) + (xcd - rem) * q;
+  count = q + (xcd < rem ? 1 : 0);
+}
+
 template <int GROUP_M>
-__device__ __forceinline__ void tile_coords(int bid, int nblk, int n_mt, int n_nt, int& mt, int& nt) {
-  const int xcd = bid & 7;
-  const int q = nblk >> 3, rem = nblk & 7;
-  const int start = xcd < rem ? xcd * (q + 1) : rem * (q + 1) + (xcd - rem) * q;
-  const int L = start + (bid >> 3);
+__device__ __forceinline__ void group_coords(int L, int n_mt, int n_nt, int& mt, int& nt) {
   const int per_group = GROUP_M * n_nt;
   const int g = L / per_group;
   const int first_m = g * GROUP_M;
@@ -65,6 +67,14 @@ __device__ __forceinline__ void tile_coords(int bid, int nblk, int n_mt, int n_n
   const int in = L - g * per_group;
   mt = first_m + in % gm;
   nt = in / gm;
+}
+
+// Workgroup id -> (m tile, n tile) for a grid of one workgroup per tile.
+template <int GROUP_M>
+__device__ __forceinline__ void tile_coords(int bid, int nblk, int n_mt, int n_nt, int& mt, int& nt) {
+  int start, count;
+  xcd_range(bid & 7, nblk, start, count);
+  group_coords<GROUP_M>(start + (bid >> 3), n_mt, n_nt, mt, nt);
 }
 
 // Main loop selectors (see the three loops below).
@@ -122,6 +132,7 @@ __device__ __forceinline__ u32x4 make_desc(const void* base, uint32_t bytes) {
 // compiler's own waits for other loads stay correct (extra outstanding loads only make a vmcnt
 // wait stricter).  M0 (the LDS destination base) is written inside the same asm block.
 __device__ __forceinline__ void dma16(u32x4 desc, uint32_t voff, uint32_t lds_base) {
+  lds_base = __builtin_amdgcn_readfirstlane(lds_base);  // wavefront-uniform by construction
   asm volatile(
       "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
@@ -353,47 +364,53 @@ __device__ __forceinline__ void tile_mainloop_spread(const __bf16* __restrict__ 
 // Group 1 waits for its A loads of step k+1 at the end of its memory phase of step k (phase 2k+1);
 // group 0 waits for its B loads of step k+1 at the end of its compute phase of step k (phase 2k+1).
 // Every barrier is preceded by the wait for the wavefront's own LDS reads, so a slot is never
-// overwritten while a read of it is in flight.
+// overwritten while a read of it is in flight.  Loads of steps past the end are not issued, so
+// when run() returns no load is in flight and a persistent caller may start() its next tile at
+// once: those first loads then travel while the caller reduces the finished tile's accumulators.
 
 template <class Cfg>
-__device__ __forceinline__ void tile_mainloop_pingpong(const __bf16* __restrict__ A, int64_t lda, int rowsA,
-                                                       const __bf16* __restrict__ B, int64_t ldb, int rowsB,
-                                                       int K, char* __restrict__ lds,
-                                                       f32x4 (&acc)[MSUB][Cfg::NSUB]) {
+struct PingPong {
   static_assert(Cfg::NWAVES == 8 && Cfg::WM == 2 && Cfg::BK == 64 && Cfg::TM == 256 && Cfg::TN == 256,
                 "ping-pong loop: 8 wavefronts, 256 x 256 tile, K = 64 steps");
-  constexpr int ROW = Cfg::ROW;                 // 128 bytes
-  constexpr int SLOT = 256 * ROW;               // 32 KB: one operand of one step
-  constexpr int B_BASE = 3 * SLOT;              // A slots 0..2, then B slots 0..1
-  constexpr int DPW = 8;                        // DMA instructions per wavefront per step (8 rows each)
-  constexpr int KSUB = Cfg::KSUB;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int group = wave >> 2;
-  const int gw = wave & 3;
-  const int wm = wave % Cfg::WM;
-  const int wn = wave / Cfg::WM;
+  static constexpr int ROW = Cfg::ROW;          // 128 bytes
+  static constexpr int SLOT = 256 * ROW;        // 32 KB: one operand of one step
+  static constexpr int B_BASE = 3 * SLOT;       // A slots 0..2, then B slots 0..1
+  static constexpr int DPW = 8;                 // DMA instructions per wavefront per step (8 rows each)
+  static constexpr int KSUB = Cfg::KSUB;
 
-  // group 1 loads A, group 0 loads B; wavefront gw of a group loads rows [64 gw, 64 gw + 64)
-  const bool loads_a = group == 1;
-  const u32x4 desc = loads_a ? make_desc(A, (uint32_t)((int64_t)rowsA * lda * 2))
-                             : make_desc(B, (uint32_t)((int64_t)rowsB * ldb * 2));
-  const int64_t ld = loads_a ? lda : ldb;
-  const uint32_t lds0 = lds_addr(lds);
-  const int dl_row = lane >> 3;
-  const int dl_pc = lane & 7;
-  const int blk0 = gw * DPW;                    // even, so block i has the parity of i
-  const int lc_even = dl_pc ^ (dl_row >> 1);    // swz(row) = (row >> 1) & 7 for row = 8 blk + dl_row
-  const int lc_odd = dl_pc ^ (4 + (dl_row >> 1));
-  const uint32_t row_off = (uint32_t)((blk0 * 8 + dl_row) * ld * 2);
-  const uint32_t blk_stride = (uint32_t)(8 * ld * 2);
-  const int nk = (K + Cfg::BK - 1) / Cfg::BK;
-  auto dma_step = [&](int kt) {   // this group's operand of step kt into its slot
-    const bool kt_in = kt < nk;
+  char* lds;
+  int lane, group, wm, wn;
+  bool loads_a;                                 // group 1 loads A, group 0 loads B
+  uint32_t lds0;
+  int blk0, lc_even, lc_odd;
+  // per tile
+  u32x4 desc;
+  uint32_t row_off, blk_stride;
+  int K, nk;
+
+  __device__ __forceinline__ PingPong(char* lds_) : lds(lds_) {
+    const int tid = threadIdx.x;
+    lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    group = wave >> 2;
+    wm = wave % Cfg::WM;
+    wn = wave / Cfg::WM;
+    loads_a = group == 1;
+    lds0 = lds_addr(lds);
+    // wavefront wave % 4 of a group loads rows [64 (wave % 4), + 64) of its operand
+    blk0 = (wave & 3) * DPW;                    // even, so block i has the parity of i
+    const int dl_row = lane >> 3;
+    const int dl_pc = lane & 7;
+    lc_even = dl_pc ^ (dl_row >> 1);            // swz(row) = (row >> 1) & 7 for row = 8 blk + dl_row
+    lc_odd = dl_pc ^ (4 + (dl_row >> 1));
+  }
+
+  // this group's operand of step kt into its slot; nothing is issued for kt >= nk
+  __device__ __forceinline__ void dma_step(int kt) const {
+    if (kt >= nk) return;
     const int k0 = kt * Cfg::BK;
-    const bool ok_even = kt_in && k0 + lc_even * 8 < K;
-    const bool ok_odd = kt_in && k0 + lc_odd * 8 < K;
+    const bool ok_even = k0 + lc_even * 8 < K;
+    const bool ok_odd = k0 + lc_odd * 8 < K;
     const uint32_t ve = row_off + lc_even * 16 + (uint32_t)kt * ROW;
     const uint32_t vo = row_off + lc_odd * 16 + (uint32_t)kt * ROW;
     const uint32_t sbase = lds0 + (loads_a ? (kt % 3) * SLOT : B_BASE + (kt & 1) * SLOT) + blk0 * 1024;
@@ -403,55 +420,89 @@ __device__ __forceinline__ void tile_mainloop_pingpong(const __bf16* __restrict_
       const uint32_t voff = ((i & 1) ? vo : ve) + (uint32_t)i * blk_stride;
       dma16(desc, ok ? voff : OOB_OFFSET, sbase + i * 1024);
     }
-  };
-
-  const int fr = lane & 15;
-  const int fsw = Cfg::swz(fr);
-  const int a_frow = (wm * WAVE_M + fr) * ROW;
-  const int b_frow = (wn * Cfg::WAVE_N + fr) * ROW;
-  bf16x8 fa[KSUB][MSUB], fb[KSUB][Cfg::NSUB];
-
-  // prologue: A of steps 0 and 1 (group 1), B of step 0 (group 0); step 0 published
-  dma_step(0);
-  if (loads_a) {
-    dma_step(1);
-    wait_vmcnt<DPW>();
-  } else {
-    wait_vmcnt<0>();
   }
-  __syncthreads();
-  if (group == 1) __syncthreads();  // group 1 runs one phase behind
 
-  for (int kt = 0; kt < nk; ++kt) {
-    // memory phase
-    dma_step(loads_a ? kt + 2 : kt + 1);
-    const char* abase = lds + (kt % 3) * SLOT;
-    const char* bbase = lds + B_BASE + (kt & 1) * SLOT;
+  // Set up a tile and issue its first loads (A of steps 0 and 1, B of step 0).  Requires every
+  // slot to be free: before the first tile, or after run() of the previous tile.
+  __device__ __forceinline__ void start(const __bf16* __restrict__ A, int64_t lda, int rowsA,
+                                        const __bf16* __restrict__ B, int64_t ldb, int rowsB, int K_) {
+    desc = loads_a ? make_desc(A, (uint32_t)((int64_t)rowsA * lda * 2))
+                   : make_desc(B, (uint32_t)((int64_t)rowsB * ldb * 2));
+    const int64_t ld = loads_a ? lda : ldb;
+    row_off = (uint32_t)((blk0 * 8 + (lane >> 3)) * ld * 2);
+    // The first steps' load offsets do not depend on the tile (the tile is in the descriptor);
+    // hiding row_off from the optimizer keeps it from hoisting them out of a persistent caller's
+    // tile loop, where they would stay live (and spill) across the K loop.
+    asm volatile("" : "+v"(row_off));
+    blk_stride = (uint32_t)(8 * ld * 2);
+    K = K_;
+    nk = (K + Cfg::BK - 1) / Cfg::BK;
+    dma_step(0);
+    if (loads_a) dma_step(1);
+  }
+
+  // The K loop of the tile set up by start().  On return every wavefront has passed the same
+  // number of barriers, every LDS read has completed and no load is in flight: all slots are free.
+  __device__ __forceinline__ void run(f32x4 (&acc)[MSUB][Cfg::NSUB]) const {
+    const int fr = lane & 15;
+    const int fsw = Cfg::swz(fr);
+    const int a_frow = (wm * WAVE_M + fr) * ROW;
+    const int b_frow = (wn * Cfg::WAVE_N + fr) * ROW;
+    bf16x8 fa[KSUB][MSUB], fb[KSUB][Cfg::NSUB];
+
+    // step 0 published (group 1 may leave A of step 1 in flight)
+    if (loads_a && nk > 1)
+      wait_vmcnt<DPW>();
+    else
+      wait_vmcnt<0>();
+    __syncthreads();
+    if (group == 1) __syncthreads();  // group 1 runs one phase behind
+
+    for (int kt = 0; kt < nk; ++kt) {
+      // memory phase
+      dma_step(loads_a ? kt + 2 : kt + 1);
+      const char* abase = lds + (kt % 3) * SLOT;
+      const char* bbase = lds + B_BASE + (kt & 1) * SLOT;
 #pragma unroll
-    for (int s = 0; s < KSUB; ++s) {
-      const int ko = Cfg::koff(s, lane, fsw);
+      for (int s = 0; s < KSUB; ++s) {
+        const int ko = Cfg::koff(s, lane, fsw);
 #pragma unroll
-      for (int m = 0; m < MSUB; ++m)
-        fa[s][m] = *reinterpret_cast<const bf16x8*>(abase + a_frow + m * MFMA_MN * ROW + ko);
+        for (int m = 0; m < MSUB; ++m)
+          fa[s][m] = *reinterpret_cast<const bf16x8*>(abase + a_frow + m * MFMA_MN * ROW + ko);
 #pragma unroll
-      for (int n = 0; n < Cfg::NSUB; ++n)
-        fb[s][n] = *reinterpret_cast<const bf16x8*>(bbase + b_frow + n * MFMA_MN * ROW + ko);
+        for (int n = 0; n < Cfg::NSUB; ++n)
+          fb[s][n] = *reinterpret_cast<const bf16x8*>(bbase + b_frow + n * MFMA_MN * ROW + ko);
+      }
+      if (loads_a) {                    // group 1's A of step kt+1 has landed
+        if (kt + 2 < nk)
+          wait_vmcnt<DPW>();
+        else
+          wait_vmcnt<0>();
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+      // compute phase
+#pragma unroll
+      for (int s = 0; s < KSUB; ++s) mfma_block<Cfg>(fa[s], fb[s], acc);
+      __builtin_amdgcn_sched_barrier(0);
+      if (!loads_a) wait_vmcnt<0>();    // group 0's B of step kt+1 has landed
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (loads_a) wait_vmcnt<DPW>();   // group 1's A of step kt+1 has landed
-    __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
-    __builtin_amdgcn_sched_barrier(0);
-    // compute phase
-#pragma unroll
-    for (int s = 0; s < KSUB; ++s) mfma_block<Cfg>(fa[s], fb[s], acc);
-    __builtin_amdgcn_sched_barrier(0);
-    if (!loads_a) wait_vmcnt<0>();    // group 0's B of step kt+1 has landed
-    __syncthreads();
-    __builtin_amdgcn_sched_barrier(0);
+    if (group == 0) __syncthreads();    // same barrier count for both groups
   }
-  if (group == 0) __syncthreads();    // same barrier count for both groups
-  wait_vmcnt<0>();                    // trailing out-of-range loads still write LDS
-  __syncthreads();
+};
+
+// One tile: start + run.
+template <class Cfg>
+__device__ __forceinline__ void tile_mainloop_pingpong(const __bf16* __restrict__ A, int64_t lda, int rowsA,
+                                                       const __bf16* __restrict__ B, int64_t ldb, int rowsB,
+                                                       int K, char* __restrict__ lds,
+                                                       f32x4 (&acc)[MSUB][Cfg::NSUB]) {
+  PingPong<Cfg> pp(lds);
+  pp.start(A, lda, rowsA, B, ldb, rowsB, K);
+  pp.run(acc);
 }
 
 }  // namespace lmh
