@@ -32,7 +32,7 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void bwd_dz_kernel(
     const float* __restrict__ grad, const float* __restrict__ lse, int T, int H, int V, int vs0, int Vc,
     int Vs, int n_mt, int n_nt, __bf16* __restrict__ dz) {
   constexpr int STAGE_OUT = Cfg::NWAVES * Cfg::WAVE_N * DZ_PITCH;
-  constexpr int LDS = Cfg::LDS_BYTES > STAGE_OUT ? Cfg::LDS_BYTES : STAGE_OUT;
+  constexpr int LDS = PingPong<Cfg>::LDS_BYTES > STAGE_OUT ? PingPong<Cfg>::LDS_BYTES : STAGE_OUT;
   __shared__ __attribute__((aligned(1024))) char lds[LDS];
   int mt, nt;
   tile_coords<8>(blockIdx.x, gridDim.x, n_mt, n_nt, mt, nt);
@@ -43,8 +43,8 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void bwd_dz_kernel(
   for (int m = 0; m < MSUB; ++m)
 #pragma unroll
     for (int n = 0; n < Cfg::NSUB; ++n) acc[m][n] = (f32x4)(0.0f);
-  tile_mainloop_pipelined<Cfg>(weight + (int64_t)(vs0 + v0) * H, H, min(Cfg::TM, Vc - v0), hidden + (int64_t)t0 * H,
-                               H, min(Cfg::TN, T - t0), H, lds, acc);
+  tile_mainloop_pingpong<Cfg>(weight + (int64_t)(vs0 + v0) * H, H, min(Cfg::TM, Vc - v0), hidden + (int64_t)t0 * H,
+                              H, min(Cfg::TN, T - t0), H, lds, acc);
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -184,8 +184,8 @@ __device__ __forceinline__ void gemm_tn_tile(const GemmProblem& p, int bid, int 
         acc[m][n][i] = (p.accumulate && row < p.M && col < p.N) ? p.C[(int64_t)row * p.ldc + col] : 0.f;
       }
 
-  tile_mainloop_pipelined<Cfg>(p.A + (int64_t)m0 * p.lda, p.lda, min(Cfg::TM, p.M - m0), p.B + (int64_t)n0 * p.ldb,
-                               p.ldb, min(Cfg::TN, p.N - n0), p.K, lds, acc);
+  tile_mainloop_pingpong<Cfg>(p.A + (int64_t)m0 * p.lda, p.lda, min(Cfg::TM, p.M - m0), p.B + (int64_t)n0 * p.ldb,
+                              p.ldb, min(Cfg::TN, p.N - n0), p.K, lds, acc);
 
 #pragma unroll
   for (int m = 0; m < MSUB; ++m)
@@ -204,7 +204,7 @@ __device__ __forceinline__ void gemm_tn_tile(const GemmProblem& p, int bid, int 
 template <class Cfg>
 __global__ __launch_bounds__(Cfg::NTHREADS) void gemm_tn_f32_kernel(GemmProblem p0, GemmProblem p1, int nblk0,
                                                                     int used0) {
-  __shared__ __attribute__((aligned(1024))) char lds[Cfg::LDS_BYTES];
+  __shared__ __attribute__((aligned(1024))) char lds[PingPong<Cfg>::LDS_BYTES];
   const int bid = blockIdx.x;
   if (bid < nblk0) {
     if (bid < used0) gemm_tn_tile<Cfg>(p0, bid, used0, lds);
@@ -257,7 +257,7 @@ BwdLayout bwd_layout(int64_t T, int64_t H, int64_t V) {
   return L;
 }
 
-// 256 x 256 tiles, 8 wavefronts (2 per SIMD), two LDS stages of K = 64, pipelined main loop
+// 256 x 256 tiles, 8 wavefronts (2 per SIMD), ping-pong main loop (160 KB of LDS)
 using CfgDz = PipeCfg<2, 4, 4, 2, 64>;
 using CfgGrad = PipeCfg<2, 4, 4, 2, 64>;
 

@@ -375,6 +375,7 @@ struct PingPong {
   static constexpr int ROW = Cfg::ROW;          // 128 bytes
   static constexpr int SLOT = 256 * ROW;        // 32 KB: one operand of one step
   static constexpr int B_BASE = 3 * SLOT;       // A slots 0..2, then B slots 0..1
+  static constexpr int LDS_BYTES = 5 * SLOT;    // 160 KB
   static constexpr int DPW = 8;                 // DMA instructions per wavefront per step (8 rows each)
   static constexpr int KSUB = Cfg::KSUB;
 
