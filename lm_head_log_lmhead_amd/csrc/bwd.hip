@@ -289,7 +289,9 @@ void launch_bwd(const BwdArgs& a, hipStream_t stream) {
       launch_transpose(a.weight + (int64_t)vs0 * L.H, L.H, Vc, L.H, wt, L.Vs, (Vc + 63) / 64 * 64, stream);
       ph = make_problem<CfgGrad>(dz, L.Vs, L.T, wt, L.Vs, L.H, Vc, a.grad_hidden, L.H, vs0 > 0 ? 1 : 0);
     }
-    launch_gemm_tn<CfgGrad>(pw, ph, stream);
+    // grad_hidden first: its tiles run K = Vs (four times the grad_weight tiles' K = T at the
+    // benchmark sizes), and dispatching the long tiles first lets the short ones fill the tail
+    launch_gemm_tn<CfgGrad>(ph, pw, stream);
   }
 }
 
