@@ -177,8 +177,9 @@ lmh_status_t lmhead_logprob_bwd(const void* hidden, const void* weight, const in
   const lmh::BwdLayout L = lmh::bwd_layout(T, H, V);
   LMH_TRY(check_ws(workspace, workspace_bytes, L.total));
   if (!grad_hidden && !grad_weight) return LMH_OK;
-  (void)hipGetLastError();
   lmh::BwdArgs a;
+  LMH_TRY(device_cus(a.cus));
+  (void)hipGetLastError();
   a.hidden = static_cast<const __bf16*>(hidden);
   a.weight = static_cast<const __bf16*>(weight);
   a.labels = labels;

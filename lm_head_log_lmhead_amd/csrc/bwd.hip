@@ -24,7 +24,8 @@ namespace lmh {
 // K3: dz tiles
 // ---------------------------------------------------------------------------------------------
 
-constexpr int DZ_PITCH = WAVE_M * 2 + 16;  // bytes per staged token row (padded against conflicts)
+constexpr int DZ_PITCH = WAVE_M * 2 + 16;
+constexpr int BWD_SCHED_WORDS = 16;        // tile counters per vocabulary step (one per XCD)  // bytes per staged token row (padded against conflicts)
 
 template <class Cfg>
 __global__ __launch_bounds__(Cfg::NTHREADS) void bwd_dz_kernel(
@@ -159,58 +160,146 @@ struct GemmProblem {
   int n_mt, n_nt;
 };
 
+// C element (row, col) of the wavefront's accumulator m, n, i: row = m0 + lane_row + 16 m + i,
+// col = n0 + lane_col + 16 n.  The per-lane parts are hidden from the optimizer so that it keeps
+// one offset per lane instead of hoisting 128 of them out of the persistent tile loop.
 template <class Cfg>
-__device__ __forceinline__ void gemm_tn_tile(const GemmProblem& p, int bid, int nblk, char* lds) {
-  int mt, nt;
-  tile_coords<8>(bid, nblk, p.n_mt, p.n_nt, mt, nt);
-  const int m0 = mt * Cfg::TM;
-  const int n0 = nt * Cfg::TN;
+__device__ __forceinline__ void c_lane_coords(int& lane_row, int& lane_col) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int wm = wave % Cfg::WM, wn = wave / Cfg::WM;
-  const int rbase = m0 + wm * WAVE_M;
-  const int cbase = n0 + wn * Cfg::WAVE_N + acc_col(lane);
-
-  // the accumulator starts at C when accumulating, so the MFMA chain continues across calls
-  f32x4 acc[MSUB][Cfg::NSUB];
-#pragma unroll
-  for (int m = 0; m < MSUB; ++m)
-#pragma unroll
-    for (int n = 0; n < Cfg::NSUB; ++n)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = rbase + m * MFMA_MN + acc_row(i, lane);
-        const int col = cbase + n * MFMA_MN;
-        acc[m][n][i] = (p.accumulate && row < p.M && col < p.N) ? p.C[(int64_t)row * p.ldc + col] : 0.f;
-      }
-
-  tile_mainloop_pingpong<Cfg>(p.A + (int64_t)m0 * p.lda, p.lda, min(Cfg::TM, p.M - m0), p.B + (int64_t)n0 * p.ldb,
-                              p.ldb, min(Cfg::TN, p.N - n0), p.K, lds, acc);
-
-#pragma unroll
-  for (int m = 0; m < MSUB; ++m)
-#pragma unroll
-    for (int n = 0; n < Cfg::NSUB; ++n)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = rbase + m * MFMA_MN + acc_row(i, lane);
-        const int col = cbase + n * MFMA_MN;
-        if (row < p.M && col < p.N) p.C[(int64_t)row * p.ldc + col] = acc[m][n][i];
-      }
+  lane_row = (wave % Cfg::WM) * WAVE_M + acc_row(0, lane);
+  lane_col = (wave / Cfg::WM) * Cfg::WAVE_N + acc_col(lane);
+  asm volatile("" : "+v"(lane_row), "+v"(lane_col));
 }
 
-// Workgroups [0, nblk0) run problem 0 and [nblk0, grid) problem 1; nblk0 is padded to a multiple
-// of 8 (padding workgroups exit at once) so both problems keep the XCD-aware tile order.
+// The accumulator starts at C when accumulating, so the MFMA chain continues across calls.
 template <class Cfg>
-__global__ __launch_bounds__(Cfg::NTHREADS) void gemm_tn_f32_kernel(GemmProblem p0, GemmProblem p1, int nblk0,
-                                                                    int used0) {
-  __shared__ __attribute__((aligned(1024))) char lds[PingPong<Cfg>::LDS_BYTES];
-  const int bid = blockIdx.x;
-  if (bid < nblk0) {
-    if (bid < used0) gemm_tn_tile<Cfg>(p0, bid, used0, lds);
-  } else {
-    gemm_tn_tile<Cfg>(p1, bid - nblk0, gridDim.x - nblk0, lds);
+__device__ __forceinline__ void gemm_acc_init(const GemmProblem& p, int m0, int n0, f32x4 (&acc)[MSUB][Cfg::NSUB]) {
+  if (!p.accumulate) {
+#pragma unroll
+    for (int m = 0; m < MSUB; ++m)
+#pragma unroll
+      for (int n = 0; n < Cfg::NSUB; ++n) acc[m][n] = (f32x4)(0.0f);
+    return;
   }
+  int lane_row, lane_col;
+  c_lane_coords<Cfg>(lane_row, lane_col);
+  const float* c = p.C + (int64_t)m0 * p.ldc + n0;
+  const int lo = lane_row * (int)p.ldc + lane_col;
+  if (m0 + Cfg::TM <= p.M && n0 + Cfg::TN <= p.N) {
+#pragma unroll
+    for (int m = 0; m < MSUB; ++m)
+#pragma unroll
+      for (int n = 0; n < Cfg::NSUB; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[m][n][i] = c[lo + (m * MFMA_MN + i) * (int)p.ldc + n * MFMA_MN];
+  } else {
+#pragma unroll
+    for (int m = 0; m < MSUB; ++m)
+#pragma unroll
+      for (int n = 0; n < Cfg::NSUB; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool ok = m0 + lane_row + m * MFMA_MN + i < p.M && n0 + lane_col + n * MFMA_MN < p.N;
+          acc[m][n][i] = ok ? c[lo + (m * MFMA_MN + i) * (int)p.ldc + n * MFMA_MN] : 0.f;
+        }
+  }
+}
+
+template <class Cfg>
+__device__ __forceinline__ void gemm_acc_store(const GemmProblem& p, int m0, int n0,
+                                               const f32x4 (&acc)[MSUB][Cfg::NSUB]) {
+  int lane_row, lane_col;
+  c_lane_coords<Cfg>(lane_row, lane_col);
+  float* c = p.C + (int64_t)m0 * p.ldc + n0;
+  const int lo = lane_row * (int)p.ldc + lane_col;
+  if (m0 + Cfg::TM <= p.M && n0 + Cfg::TN <= p.N) {
+#pragma unroll
+    for (int m = 0; m < MSUB; ++m)
+#pragma unroll
+      for (int n = 0; n < Cfg::NSUB; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) c[lo + (m * MFMA_MN + i) * (int)p.ldc + n * MFMA_MN] = acc[m][n][i];
+  } else {
+#pragma unroll
+    for (int m = 0; m < MSUB; ++m)
+#pragma unroll
+      for (int n = 0; n < Cfg::NSUB; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (m0 + lane_row + m * MFMA_MN + i < p.M && n0 + lane_col + n * MFMA_MN < p.N)
+            c[lo + (m * MFMA_MN + i) * (int)p.ldc + n * MFMA_MN] = acc[m][n][i];
+  }
+}
+
+// Persistent grid over both problems, one workgroup per CU, tiles from a TileQueue: problem 0's
+// tiles are handed out first (the launcher puts the long-K problem there), so the short tiles
+// fill the end.  As in the forward, the next tile's first loads are issued before the finished
+// tile's results are stored, and the claim of the tile after next is read a tile later.
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::NTHREADS) void gemm_tn_f32_persistent_kernel(GemmProblem p0, GemmProblem p1,
+                                                                               int* __restrict__ sched) {
+  __shared__ __attribute__((aligned(1024))) char lds[PingPong<Cfg>::LDS_BYTES];
+  // tile numbers pass from thread 0 to the workgroup through the first word of B slot 1 (see the
+  // forward's persistent kernel)
+  int* const bc = reinterpret_cast<int*>(lds + PingPong<Cfg>::B_BASE + PingPong<Cfg>::SLOT);
+  const int nt0 = p0.M > 0 ? p0.n_mt * p0.n_nt : 0;
+  const int nt1 = p1.M > 0 ? p1.n_mt * p1.n_nt : 0;
+  const TileQueue q{sched, nt0, nt1};
+  const int xcd = blockIdx.x & 7;
+  if (threadIdx.x == 0) bc[0] = q.resolve(xcd, q.claim(xcd));
+  __syncthreads();
+  int t = bc[0];
+  if (t < 0) return;
+
+  // tile t -> problem and origin
+  auto locate = [&](int tile, bool& second, int& m0, int& n0) {
+    second = tile >= nt0;
+    const GemmProblem& p = second ? p1 : p0;
+    int mt, nt;
+    group_coords<8>(second ? tile - nt0 : tile, p.n_mt, p.n_nt, mt, nt);
+    m0 = mt * Cfg::TM;
+    n0 = nt * Cfg::TN;
+  };
+  auto start = [&](PingPong<Cfg>& pp, bool second, int m0, int n0) {
+    const GemmProblem& p = second ? p1 : p0;
+    pp.start(p.A + (int64_t)m0 * p.lda, p.lda, min(Cfg::TM, p.M - m0), p.B + (int64_t)n0 * p.ldb, p.ldb,
+             min(Cfg::TN, p.N - n0), p.K);
+  };
+
+  PingPong<Cfg> pp(lds);
+  bool second;
+  int m0, n0;
+  locate(t, second, m0, n0);
+  start(pp, second, m0, n0);
+  int claim = 0;
+  if (threadIdx.x == 0) claim = q.claim(xcd);
+  for (;;) {
+    f32x4 acc[MSUB][Cfg::NSUB];
+    gemm_acc_init<Cfg>(second ? p1 : p0, m0, n0, acc);
+    pp.run(acc);
+    if (threadIdx.x == 0) bc[0] = q.resolve(xcd, claim);
+    __syncthreads();
+    const int tn = bc[0];
+    __builtin_amdgcn_sched_barrier(0);
+    bool second_n = false;
+    int m0n = 0, n0n = 0;
+    if (tn >= 0) {
+      locate(tn, second_n, m0n, n0n);
+      start(pp, second_n, m0n, n0n);
+      if (threadIdx.x == 0) claim = q.claim(xcd);
+    }
+    gemm_acc_store<Cfg>(second ? p1 : p0, m0, n0, acc);
+    if (tn < 0) break;
+    second = second_n;
+    m0 = m0n;
+    n0 = n0n;
+  }
+}
+
+__global__ void bwd_sched_reset_kernel(int* __restrict__ sched, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) sched[i] = 0;
 }
 
 template <class Cfg>
@@ -220,14 +309,14 @@ static GemmProblem make_problem(const __bf16* A, int64_t lda, int M, const __bf1
   return p;
 }
 
-// Launches one or two problems (p1.M == 0: none) in a single grid.
+// Launches one or two problems (M == 0: none) in a single persistent grid.
 template <class Cfg>
-static void launch_gemm_tn(const GemmProblem& p0, const GemmProblem& p1, hipStream_t stream) {
-  const int used0 = p0.M > 0 ? p0.n_mt * p0.n_nt : 0;
+static void launch_gemm_tn(const GemmProblem& p0, const GemmProblem& p1, int* sched, int cus, hipStream_t stream) {
+  const int n0 = p0.M > 0 ? p0.n_mt * p0.n_nt : 0;
   const int n1 = p1.M > 0 ? p1.n_mt * p1.n_nt : 0;
-  const int nblk0 = (used0 + 7) / 8 * 8;
-  if (used0 + n1 == 0) return;
-  hipLaunchKernelGGL(gemm_tn_f32_kernel<Cfg>, dim3(nblk0 + n1), dim3(Cfg::NTHREADS), 0, stream, p0, p1, nblk0, used0);
+  if (n0 + n1 == 0) return;
+  hipLaunchKernelGGL(gemm_tn_f32_persistent_kernel<Cfg>, dim3(min(n0 + n1, cus)), dim3(Cfg::NTHREADS), 0, stream, p0,
+                     p1, sched);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -253,6 +342,9 @@ BwdLayout bwd_layout(int64_t T, int64_t H, int64_t V) {
   off += align256((size_t)H * L.Vs * 2);
   L.off_ht = off;
   off += align256((size_t)H * L.Tp * 2);
+  L.nsteps = (int)((V + L.Vs - 1) / L.Vs);
+  L.off_sched = off;
+  off += align256((size_t)L.nsteps * BWD_SCHED_WORDS * sizeof(int));
   L.total = off;
   return L;
 }
@@ -267,7 +359,12 @@ void launch_bwd(const BwdArgs& a, hipStream_t stream) {
   __bf16* dzt = reinterpret_cast<__bf16*>(a.ws + L.off_dzt);
   __bf16* wt = reinterpret_cast<__bf16*>(a.ws + L.off_wt);
   __bf16* ht = reinterpret_cast<__bf16*>(a.ws + L.off_ht);
+  int* sched = reinterpret_cast<int*>(a.ws + L.off_sched);
   if (!a.grad_hidden && !a.grad_weight) return;
+  {
+    const int n = L.nsteps * BWD_SCHED_WORDS;
+    hipLaunchKernelGGL(bwd_sched_reset_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, sched, n);
+  }
   if (a.grad_weight) launch_transpose(a.hidden, L.H, L.T, L.H, ht, L.Tp, L.Tp, stream);
 
   for (int vs0 = 0; vs0 < L.V; vs0 += L.Vs) {
@@ -291,7 +388,7 @@ void launch_bwd(const BwdArgs& a, hipStream_t stream) {
     }
     // grad_hidden first: its tiles run K = Vs (four times the grad_weight tiles' K = T at the
     // benchmark sizes), and dispatching the long tiles first lets the short ones fill the tail
-    launch_gemm_tn<CfgGrad>(ph, pw, stream);
+    launch_gemm_tn<CfgGrad>(ph, pw, sched + (vs0 / L.Vs) * BWD_SCHED_WORDS, a.cus, stream);
   }
 }
 

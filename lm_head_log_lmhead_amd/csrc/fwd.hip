@@ -192,10 +192,10 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void fwd_partials_kernel(
 
 // Persistent form for the ping-pong tile: one workgroup per CU.
 //
-// Tiles are handed out by per-XCD counters in the workspace.  A workgroup on XCD x takes the next
-// tile of x's contiguous tile range (so the workgroups of an XCD work on neighbouring tiles
-// together, sharing A and B rows in that XCD's L2); once x's range is used up it takes tiles from
-// the other XCDs' ranges.  XCDs do not run at the same speed, and a static split leaves the fastest
+// Tiles are handed out by a TileQueue over per-XCD counters in the workspace.  A workgroup on XCD
+// x takes the next tile of x's contiguous tile range (so the workgroups of an XCD work on
+// neighbouring tiles together, sharing A and B rows in that XCD's L2); once x's range is used up
+// it takes tiles from the other XCDs' ranges.  XCDs do not run at the same speed, and a static split leaves the fastest
 // idle at the end.  The counters decide only which workgroup computes a tile, never what it
 // computes: every tile's records are the same bits whoever computes them.
 //
@@ -203,18 +203,6 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void fwd_partials_kernel(
 // the next tile's K loop, so its latency hides behind that loop.  The next tile's first loads are
 // issued before the finished tile's records are computed, so their latency hides behind that VALU
 // work, and no workgroup launch separates the tiles.
-
-// Thread 0: a tile from another XCD's range, or -1 when every range is used up.
-__device__ __noinline__ int steal_tile(int* sched, int xcd, int ntiles) {
-  for (int k = 1; k < 8; ++k) {
-    const int x = (xcd + k) & 7;
-    int start, count;
-    xcd_range(x, ntiles, start, count);
-    const int i = atomicAdd(&sched[x], 1);
-    if (i < count) return start + i;
-  }
-  return -1;
-}
 
 __global__ void fwd_sched_reset_kernel(int* __restrict__ sched) {
   if (threadIdx.x < SCHED_WORDS) sched[threadIdx.x] = 0;
@@ -229,16 +217,13 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void fwd_partials_persistent_kernel(
   // Tile numbers are passed from thread 0 to the workgroup through the first word of B slot 1,
   // which no load writes between the end of one K loop and the first barrier of the next.
   int* const bc = reinterpret_cast<int*>(lds + PingPong<Cfg>::B_BASE + PingPong<Cfg>::SLOT);
-  const int ntiles = n_mt * n_nt;
+  const TileQueue q{sched, n_mt * n_nt, 0};
   const int xcd = blockIdx.x & 7;
-  int xs, xc;
-  xcd_range(xcd, ntiles, xs, xc);
   const int wm = (threadIdx.x >> 6) % Cfg::WM;
   const int wn = (threadIdx.x >> 6) / Cfg::WM;
   const int lane = threadIdx.x & 63;
 
-  auto own_or_steal = [&](int i) { return i < xc ? xs + i : steal_tile(sched, xcd, ntiles); };
-  if (threadIdx.x == 0) bc[0] = own_or_steal(atomicAdd(&sched[xcd], 1));
+  if (threadIdx.x == 0) bc[0] = q.resolve(xcd, q.claim(xcd));
   __syncthreads();
   int L = bc[0];
   if (L < 0) return;
@@ -249,7 +234,7 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void fwd_partials_persistent_kernel(
   int v0 = mt * Cfg::TM, t0 = nt * Cfg::TN;
   pp.start(weight + (int64_t)v0 * H, H, min(Cfg::TM, V - v0), hidden + (int64_t)t0 * H, H, min(Cfg::TN, T - t0), H);
   int claim = 0;  // thread 0: raw counter value of the next claim on this XCD's range
-  if (threadIdx.x == 0) claim = atomicAdd(&sched[xcd], 1);
+  if (threadIdx.x == 0) claim = q.claim(xcd);
   for (;;) {
     int y[Cfg::NSUB];
     load_labels(labels, t0 + wn * Cfg::WAVE_N, lane, T, y);
@@ -263,7 +248,7 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void fwd_partials_persistent_kernel(
     // them then covers nothing else.
     int lw[Cfg::NSUB];
     label_offsets(y, v0 + wm * WAVE_M, V, lw);
-    if (threadIdx.x == 0) bc[0] = own_or_steal(claim);
+    if (threadIdx.x == 0) bc[0] = q.resolve(xcd, claim);
     __syncthreads();
     const int Ln = bc[0];
     __builtin_amdgcn_sched_barrier(0);
@@ -274,7 +259,7 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void fwd_partials_persistent_kernel(
       t0n = nt * Cfg::TN;
       pp.start(weight + (int64_t)v0n * H, H, min(Cfg::TM, V - v0n), hidden + (int64_t)t0n * H, H,
                min(Cfg::TN, T - t0n), H);
-      if (threadIdx.x == 0) claim = atomicAdd(&sched[xcd], 1);
+      if (threadIdx.x == 0) claim = q.claim(xcd);
     }
     tile_records<Cfg>(acc, v0, t0, T, V, lw, rec, zy);
     if (Ln < 0) break;

@@ -40,7 +40,8 @@ struct BwdLayout {
   int T, H, V;
   int Tp;      // T rounded up to 64 (pitch of the transposed token-major buffers)
   int Vs;      // vocabulary rows per step: min(BWD_VOCAB_STEP, V rounded up to 256)
-  size_t off_dz, off_dzt, off_wt, off_ht, total;
+  int nsteps;  // ceil(V / Vs)
+  size_t off_dz, off_dzt, off_wt, off_ht, off_sched, total;
 };
 
 BwdLayout bwd_layout(int64_t T, int64_t H, int64_t V);
@@ -56,6 +57,7 @@ struct BwdArgs {
   int accumulate_gw;
   char* ws;
   BwdLayout L;
+  int cus;      // compute units of the device (persistent grids)
 };
 
 void launch_bwd(const BwdArgs& a, hipStream_t stream);

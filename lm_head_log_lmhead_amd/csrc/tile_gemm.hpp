@@ -77,6 +77,38 @@ __device__ __forceinline__ void tile_coords(int bid, int nblk, int n_mt, int n_n
   group_coords<GROUP_M>(start + (bid >> 3), n_mt, n_nt, mt, nt);
 }
 
+// Dynamic tile queue of a persistent grid over one or two problems (problem 0's tiles are handed
+// out before problem 1's).  Each XCD owns a contiguous share of each problem (xcd_range) and a
+// counter ctr[x] in device memory, zeroed before the launch; counter value i on XCD x is the i-th
+// tile of x's list "problem-0 share, then problem-1 share".  A workgroup on XCD x claims from
+// ctr[x] and, once x's list is used up, from the other XCDs' counters.  Tiles are numbered
+// 0 .. n0-1 for problem 0 and n0 .. n0+n1-1 for problem 1; -1 means no tile is left.  The queue
+// decides only which workgroup computes a tile.  Only one thread per workgroup calls it.
+struct TileQueue {
+  int* ctr;
+  int n0, n1;
+
+  __device__ __forceinline__ int decode(int x, int i) const {
+    int s0, c0, s1, c1;
+    xcd_range(x, n0, s0, c0);
+    if (i < c0) return s0 + i;
+    xcd_range(x, n1, s1, c1);
+    i -= c0;
+    return i < c1 ? n0 + s1 + i : -1;
+  }
+  // raw claim on the own XCD's list (its result may be read much later)
+  __device__ __forceinline__ int claim(int x) const { return atomicAdd(&ctr[x], 1); }
+  // the tile of a raw claim, stealing from the other XCDs when the own list is used up
+  __device__ __forceinline__ int resolve(int x, int raw) const {
+    int t = decode(x, raw);
+    for (int k = 1; t < 0 && k < 8; ++k) {
+      const int y = (x + k) & 7;
+      t = decode(y, atomicAdd(&ctr[y], 1));
+    }
+    return t;
+  }
+};
+
 // Main loop selectors (see the three loops below).
 constexpr int LOOP_PIPELINED = 0;
 constexpr int LOOP_SPREAD = 1;
