@@ -179,10 +179,8 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void fwd_partials_kernel(
   const __bf16* A = weight + (int64_t)v0 * H;
   const __bf16* B = hidden + (int64_t)t0 * H;
   const int rowsA = min(Cfg::TM, V - v0), rowsB = min(Cfg::TN, T - t0);
-  if constexpr (Cfg::LOOP == LOOP_SPREAD)
-    tile_mainloop_spread<Cfg>(A, H, rowsA, B, H, rowsB, H, lds, acc);
-  else
-    tile_mainloop_pipelined<Cfg>(A, H, rowsA, B, H, rowsB, H, lds, acc);
+  static_assert(Cfg::LOOP == LOOP_SPREAD, "one-tile-per-workgroup grid: spread main loop");
+  tile_mainloop_spread<Cfg>(A, H, rowsA, B, H, rowsB, H, lds, acc);
   const int wave = threadIdx.x >> 6;
   int y[Cfg::NSUB], lw[Cfg::NSUB];
   load_labels(labels, t0 + (wave / Cfg::WM) * Cfg::WAVE_N, threadIdx.x & 63, T, y);
@@ -393,11 +391,11 @@ struct FwdCfg : P {
   static constexpr int LDS_BYTES = LOOP_ == LOOP_PINGPONG ? 5 * 256 * P::ROW : P::LDS_BYTES;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
-// T > 1024: 256 vocab x 256 tokens, 8 wavefronts (2 per SIMD) in two groups that alternate between
-// loads and MFMAs, K = 64 steps, three A slots and two B slots (160 KB of LDS)
+// T > 64: 256 vocab x 256 tokens, 8 wavefronts (2 per SIMD) in two groups that alternate between
+// loads and MFMAs, K = 64 steps, three A slots and two B slots (160 KB of LDS), persistent grid.
+// From T = 96 up it beat a 4-wavefront 256 x 128 tile everywhere measured, even where most of
+// its token columns are empty: the weight stream, not the MFMA work, sets the time there.
 using CfgBig = FwdCfg<PipeCfg<2, 4, 4, 2, 64>, LOOP_PINGPONG>;
-// 64 < T <= 1024: 256 vocab x 128 tokens, 4 wavefronts, three stages of K = 64
-using CfgMid = FwdCfg<PipeCfg<2, 2, 4, 3, 64>, LOOP_PIPELINED>;
 // T <= 32: 256 vocab x 32 tokens, 2 wavefronts, four stages of K = 64 with the loads spread between
 // the MFMAs: the weight stream is HBM-bound here, so deep prefetch matters most
 using CfgSmall = FwdCfg<PipeCfg<2, 1, 2, LMH_SMALL_NS, LMH_SMALL_BK>, LOOP_SPREAD>;
@@ -409,8 +407,6 @@ void launch_fwd_partials(const FwdArgs& a, hipStream_t stream) {
     launch_partials_cfg<CfgSmall>(a, stream);
   else if (a.T <= 64)
     launch_partials_cfg<CfgS64>(a, stream);
-  else if (a.T <= 1024)
-    launch_partials_cfg<CfgMid>(a, stream);
   else
     launch_partials_cfg<CfgBig>(a, stream);
 }

@@ -109,8 +109,7 @@ struct TileQueue {
   }
 };
 
-// Main loop selectors (see the three loops below).
-constexpr int LOOP_PIPELINED = 0;
+// Main loop selectors (see the two loops below).
 constexpr int LOOP_SPREAD = 1;
 constexpr int LOOP_PINGPONG = 2;
 
@@ -243,69 +242,6 @@ __device__ __forceinline__ void mfma_block(const bf16x8 (&af)[MSUB], const bf16x
   for (int m = 0; m < MSUB; ++m)
 #pragma unroll
     for (int n = 0; n < Cfg::NSUB; ++n) acc[m][n] = mfma(af[m], bfr[n], acc[m][n]);
-}
-
-// =============================================================================================
-// LOOP_PIPELINED: a ring of NS stages with software-pipelined fragments.
-// =============================================================================================
-//
-// The fragments are double buffered in registers: the ds_reads of k-slice s+1 are in flight
-// while the MFMAs of slice s run, and the step's barrier sits between the last ds_read of the
-// step and its last MFMAs, so the matrix pipe keeps working across the barrier and the first
-// fragments of the next step load under those MFMAs.  Stage kt is refilled with step kt+NS right
-// after that barrier (every read of stage kt has been issued by then), so NS = 2 stages of K = 64
-// already give each load one step of slack.
-
-template <class Cfg>
-__device__ __forceinline__ void tile_mainloop_pipelined(const __bf16* __restrict__ A, int64_t lda, int rowsA,
-                                                        const __bf16* __restrict__ B, int64_t ldb, int rowsB,
-                                                        int K, char* __restrict__ lds,
-                                                        f32x4 (&acc)[MSUB][Cfg::NSUB]) {
-  constexpr int ROW = Cfg::ROW;
-  constexpr int KSUB = Cfg::KSUB;
-  constexpr int NS = Cfg::NS;
-  constexpr int IPW = RingDma<Cfg>::NDMA;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave % Cfg::WM;
-  const int wn = wave / Cfg::WM;
-  const RingDma<Cfg> ring(A, lda, rowsA, B, ldb, rowsB, K, lds, wave, lane);
-
-  const int fr = lane & 15;
-  const int fsw = Cfg::swz(fr);
-  const int a_frow = (wm * WAVE_M + fr) * ROW;
-  const int b_frow = Cfg::TM * ROW + (wn * Cfg::WAVE_N + fr) * ROW;
-  int koff[KSUB];
-#pragma unroll
-  for (int s = 0; s < KSUB; ++s) koff[s] = Cfg::koff(s, lane, fsw);
-
-  // prologue: steps 0..NS-1 in flight, wait for step 0
-#pragma unroll
-  for (int p = 0; p < NS; ++p) ring.step(p, wave);
-  wait_vmcnt<(NS - 1) * IPW>();
-  __syncthreads();
-  bf16x8 fa[2][MSUB], fb[2][Cfg::NSUB];
-  load_frags<Cfg>(lds, a_frow, b_frow, koff[0], fa[0], fb[0]);
-
-  for (int kt = 0; kt < ring.nk; ++kt) {
-    const char* base = lds + (kt % NS) * Cfg::STAGE_BYTES;
-    const char* nbase = lds + ((kt + 1) % NS) * Cfg::STAGE_BYTES;
-#pragma unroll
-    for (int s = 0; s < KSUB - 1; ++s) {
-      load_frags<Cfg>(base, a_frow, b_frow, koff[s + 1], fa[(s + 1) & 1], fb[(s + 1) & 1]);
-      mfma_block<Cfg>(fa[s & 1], fb[s & 1], acc);
-    }
-    // Every read of stage kt has been issued (the barrier waits for them): publish step kt+1
-    // (its loads were issued NS-1 steps ago) and refill stage kt with step kt+NS.
-    wait_vmcnt<(NS - 2) * IPW>();
-    __syncthreads();
-    ring.step(kt + NS, wave);
-    if (kt + 1 < ring.nk) load_frags<Cfg>(nbase, a_frow, b_frow, koff[0], fa[0], fb[0]);
-    mfma_block<Cfg>(fa[(KSUB - 1) & 1], fb[(KSUB - 1) & 1], acc);
-  }
-  wait_vmcnt<0>();   // trailing out-of-range loads still write LDS
-  __syncthreads();
 }
 
 // =============================================================================================
