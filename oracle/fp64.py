@@ -28,14 +28,32 @@ What is computed, and where the pages define it:
   the -softmax term remains and the onehot term drops; streaming-backward commit: exp of the
   log-softmax, negate, multiply by the upstream gradient, then add it at the label).
   ``grad_hidden = dz @ W`` and ``grad_weight = dz^T @ h``.
+* Temperature ``tau``: the logits are divided by it before the log-softmax, so every quantity
+  above is that of ``softmax(z / tau)``, and the backward carries the chain-rule factor 1/tau.
+  The division is of the full-precision logits by the caller's fp32 temperature, never by a
+  bf16-rounded one (verl PR #8026, review on the temperature order: the sampler divides fp32
+  logits by the fp32 temperature, and doing it on bf16 logits with a bf16 temperature changes
+  every token).  Here the logits are fp64 and ``tau`` is the given value widened exactly.
+* ``sum_p2_t = sum_j p_tj^2`` of the same softmax, a companion metric of the entropy that the
+  pages compute from the same logits (verl PR #8026, first review and its follow-up: entropy and
+  sum_pi_squared are kept next to the log-probs).
+* Entropy gradient, which the pages leave unwired (SkyRL PR #1765, PR summary: entropy stays
+  no-grad until its gradient is wired and validated): for ``sum_t gE_t * entropy_t`` the logit
+  gradient is ``-gE_t * p_tj * (log p_tj + entropy_t)`` (with ``log p = z/tau - lse``), added to
+  the log-prob term before the 1/tau factor.
 
 Parity pins (tests/test_oracle_pins.py): agreement with the scalar ``math.fsum`` oracle in
 ``oracle.brute`` on tiny shapes; sum_j exp(logprob_j) = 1; uniform logits give -log V and log V;
 V = 1 and V = 2 closed forms; shift invariance; a one-hot design with exactly known logits; the
 peaked-row closed form of the entropy; central finite differences of the backward; the ``h = 0``
-closed form of both gradients; the column sums of ``grad_weight``.  No function here is unpinned.
+closed form of both gradients; the column sums of ``grad_weight``; with a temperature, the
+one-hot, two-entry and infinite-temperature closed forms and finite differences; for
+``sum_p2``, the one-hot and uniform closed forms; for the entropy gradient, finite differences of
+the entropy.  No function here is unpinned.
 """
 from __future__ import annotations
+
+import math
 
 import numpy as np
 import torch
@@ -56,14 +74,26 @@ def _labels(y) -> np.ndarray:
     return np.asarray(y, dtype=np.int64)
 
 
-def _block_softmax_terms(hb: np.ndarray, W: np.ndarray):
-    """Full logits of a block of rows and their log-softmax: returns (z, lse, logp)."""
-    z = hb @ W.T                                    # [rows, V]
+def _temperature(temperature) -> float:
+    tau = float(temperature)
+    if not (math.isfinite(tau) and tau > 0.0):
+        raise ValueError(f"temperature must be finite and positive, got {temperature!r}")
+    return tau
+
+
+def _block_softmax_terms(hb: np.ndarray, W: np.ndarray, tau: float = 1.0):
+    """Full logits of a block of rows, divided by the temperature, and their log-softmax:
+    returns (z, lse, logp)."""
+    z = (hb @ W.T) / tau                            # [rows, V]
     M = z.max(axis=1)
     S = np.exp(z - M[:, None]).sum(axis=1)
     lse = M + np.log(S)
     logp = z - lse[:, None]
     return z, lse, logp
+
+
+def _sum_p2(p: np.ndarray) -> np.ndarray:
+    return (p * p).sum(axis=1)
 
 
 def _gather_label(logp: np.ndarray, yb: np.ndarray, V: int) -> np.ndarray:
@@ -75,15 +105,16 @@ def _gather_label(logp: np.ndarray, yb: np.ndarray, V: int) -> np.ndarray:
 
 
 def forward_rows(hidden, weight, labels, rows=None, entropy: bool = True,
-                 row_block: int = DEFAULT_ROW_BLOCK) -> dict:
+                 row_block: int = DEFAULT_ROW_BLOCK, temperature=1.0, sum_p2: bool = False) -> dict:
     """Forward for the selected token rows (all rows if ``rows`` is None).
 
-    Returns a dict of float64 arrays: ``logprob``, ``lse`` and (if asked) ``entropy``, indexed like
-    ``rows``.
+    Returns a dict of float64 arrays: ``logprob``, ``lse`` and, if asked, ``entropy`` and
+    ``sum_p2``, indexed like ``rows``.  ``lse`` is that of the logits divided by the temperature.
     """
     h = to_f64(hidden)
     W = to_f64(weight)
     y = _labels(labels)
+    tau = _temperature(temperature)
     V = W.shape[0]
     if rows is None:
         rows = np.arange(h.shape[0])
@@ -92,81 +123,106 @@ def forward_rows(hidden, weight, labels, rows=None, entropy: bool = True,
     lp = np.zeros(n)
     lse = np.zeros(n)
     ent = np.zeros(n) if entropy else None
+    p2 = np.zeros(n) if sum_p2 else None
     for s in range(0, n, row_block):
         rb = rows[s:s + row_block]
-        _, lse_b, logp = _block_softmax_terms(h[rb], W)
+        _, lse_b, logp = _block_softmax_terms(h[rb], W, tau)
         lse[s:s + len(rb)] = lse_b
         lp[s:s + len(rb)] = _gather_label(logp, y[rb], V)
-        if entropy:
+        if entropy or sum_p2:
             p = np.exp(logp)
+        if entropy:
             ent[s:s + len(rb)] = -(p * logp).sum(axis=1)
+        if sum_p2:
+            p2[s:s + len(rb)] = _sum_p2(p)
     out = {"logprob": lp, "lse": lse}
     if entropy:
         out["entropy"] = ent
+    if sum_p2:
+        out["sum_p2"] = p2
     return out
 
 
-def forward(hidden, weight, labels, entropy: bool = True, row_block: int = DEFAULT_ROW_BLOCK) -> dict:
-    """Forward over every row: ``logprob[T]``, ``lse[T]``, ``entropy[T]`` (float64)."""
-    return forward_rows(hidden, weight, labels, None, entropy, row_block)
+def forward(hidden, weight, labels, entropy: bool = True, row_block: int = DEFAULT_ROW_BLOCK,
+            temperature=1.0, sum_p2: bool = False) -> dict:
+    """Forward over every row: ``logprob[T]``, ``lse[T]``, ``entropy[T]`` (and ``sum_p2[T]`` if
+    asked), float64."""
+    return forward_rows(hidden, weight, labels, None, entropy, row_block, temperature, sum_p2)
 
 
-def _dz_block(logp: np.ndarray, yb: np.ndarray, gb: np.ndarray, V: int) -> np.ndarray:
-    """dz = g * (onehot(y) - p); the onehot term is absent for labels outside [0, V)."""
-    dz = -np.exp(logp) * gb[:, None]
+def _dz_block(logp: np.ndarray, yb: np.ndarray, gb: np.ndarray, V: int, tau: float = 1.0,
+              ge: np.ndarray | None = None) -> np.ndarray:
+    """Logit gradient of sum_t g_t logprob_t (+ sum_t ge_t entropy_t):
+    (g * (onehot(y) - p) - ge * p * (log p + entropy)) / tau; the onehot term is absent for labels
+    outside [0, V)."""
+    p = np.exp(logp)
+    dz = -p * gb[:, None]
     valid = (yb >= 0) & (yb < V)
     r = np.nonzero(valid)[0]
     dz[r, yb[r]] += gb[r]
-    return dz
+    if ge is not None:
+        ent = -(p * logp).sum(axis=1)
+        dz -= ge[:, None] * p * (logp + ent[:, None])
+    return dz / tau
 
 
-def backward(hidden, weight, labels, grad, row_block: int = DEFAULT_ROW_BLOCK):
-    """Gradients of ``sum_t grad_t * logprob_t``: returns (grad_hidden [T,H], grad_weight [V,H])."""
+def backward(hidden, weight, labels, grad, row_block: int = DEFAULT_ROW_BLOCK, temperature=1.0,
+             grad_entropy=None):
+    """Gradients of ``sum_t grad_t * logprob_t`` (+ ``sum_t grad_entropy_t * entropy_t``):
+    returns (grad_hidden [T,H], grad_weight [V,H])."""
     h = to_f64(hidden)
     W = to_f64(weight)
     y = _labels(labels)
     g = to_f64(grad)
+    ge = None if grad_entropy is None else to_f64(grad_entropy)
+    tau = _temperature(temperature)
     T, V = h.shape[0], W.shape[0]
     gh = np.zeros_like(h)
     gW = np.zeros_like(W)
     for s in range(0, T, row_block):
         sl = slice(s, min(T, s + row_block))
-        _, _, logp = _block_softmax_terms(h[sl], W)
-        dz = _dz_block(logp, y[sl], g[sl], V)
+        _, _, logp = _block_softmax_terms(h[sl], W, tau)
+        dz = _dz_block(logp, y[sl], g[sl], V, tau, None if ge is None else ge[sl])
         gh[sl] = dz @ W
         gW += dz.T @ h[sl]
     return gh, gW
 
 
-def grad_hidden_rows(hidden, weight, labels, grad, rows, row_block: int = DEFAULT_ROW_BLOCK) -> np.ndarray:
+def grad_hidden_rows(hidden, weight, labels, grad, rows, row_block: int = DEFAULT_ROW_BLOCK, temperature=1.0,
+                     grad_entropy=None) -> np.ndarray:
     """grad_hidden for the selected token rows only (each row needs only its own logits)."""
     h = to_f64(hidden)
     W = to_f64(weight)
     y = _labels(labels)
     g = to_f64(grad)
+    ge = None if grad_entropy is None else to_f64(grad_entropy)
+    tau = _temperature(temperature)
     V = W.shape[0]
     rows = np.asarray(rows, dtype=np.int64)
     out = np.zeros((rows.shape[0], h.shape[1]))
     for s in range(0, rows.shape[0], row_block):
         rb = rows[s:s + row_block]
-        _, _, logp = _block_softmax_terms(h[rb], W)
-        out[s:s + len(rb)] = _dz_block(logp, y[rb], g[rb], V) @ W
+        _, _, logp = _block_softmax_terms(h[rb], W, tau)
+        out[s:s + len(rb)] = _dz_block(logp, y[rb], g[rb], V, tau, None if ge is None else ge[rb]) @ W
     return out
 
 
-def grad_weight_rows(hidden, weight, labels, grad, vocab_rows, row_block: int = DEFAULT_ROW_BLOCK) -> np.ndarray:
+def grad_weight_rows(hidden, weight, labels, grad, vocab_rows, row_block: int = DEFAULT_ROW_BLOCK,
+                     temperature=1.0, grad_entropy=None) -> np.ndarray:
     """grad_weight for the selected vocabulary rows.  Every token's log-sum-exp is needed, so this
     makes one full pass over the logits."""
     h = to_f64(hidden)
     W = to_f64(weight)
     y = _labels(labels)
     g = to_f64(grad)
+    ge = None if grad_entropy is None else to_f64(grad_entropy)
+    tau = _temperature(temperature)
     T, V = h.shape[0], W.shape[0]
     vr = np.asarray(vocab_rows, dtype=np.int64)
     out = np.zeros((vr.shape[0], h.shape[1]))
     for s in range(0, T, row_block):
         sl = slice(s, min(T, s + row_block))
-        _, _, logp = _block_softmax_terms(h[sl], W)
-        dz = _dz_block(logp, y[sl], g[sl], V)
+        _, _, logp = _block_softmax_terms(h[sl], W, tau)
+        dz = _dz_block(logp, y[sl], g[sl], V, tau, None if ge is None else ge[sl])
         out += dz[:, vr].T @ h[sl]
     return out

@@ -10,16 +10,16 @@ from oracle import fp64
 from tests import test_oracle_pins as pins
 
 
-def _terms_transposed_shift(hb, W):
-    z = hb @ W.T
+def _terms_transposed_shift(hb, W, tau=1.0):
+    z = hb @ W.T / tau
     M = z.max(axis=1)
     S = np.exp(z - M[:, None]).sum(axis=1)
     lse = M + np.log(S)
     return z, lse, z - lse[:, None] + 1e-3        # off by a constant
 
 
-def _terms_no_max(hb, W):
-    z = hb @ W.T
+def _terms_no_max(hb, W, tau=1.0):
+    z = hb @ W.T / tau
     M = z.max(axis=1)
     S = np.exp(z - M[:, None]).sum(axis=1)
     lse = np.log(S)                                # dropped the max term
@@ -34,16 +34,50 @@ def _gather_next(logp, yb, V):
     return out
 
 
-def _dz_sign(logp, yb, gb, V):
+def _dz_sign(logp, yb, gb, V, tau=1.0, ge=None):
     dz = np.exp(logp) * gb[:, None]                # wrong sign of the softmax term
     valid = (yb >= 0) & (yb < V)
     r = np.nonzero(valid)[0]
     dz[r, yb[r]] += gb[r]
-    return dz
+    return dz / tau
 
 
-def _dz_no_onehot(logp, yb, gb, V):
-    return -np.exp(logp) * gb[:, None]             # dropped the label term
+def _dz_no_onehot(logp, yb, gb, V, tau=1.0, ge=None):
+    return -np.exp(logp) * gb[:, None] / tau       # dropped the label term
+
+
+def _terms_times_tau(hb, W, tau=1.0):
+    z = hb @ W.T * tau                             # multiplied instead of divided
+    M = z.max(axis=1)
+    S = np.exp(z - M[:, None]).sum(axis=1)
+    lse = M + np.log(S)
+    return z, lse, z - lse[:, None]
+
+
+_dz_right = fp64._dz_block
+
+
+def _dz_no_tau(logp, yb, gb, V, tau=1.0, ge=None):
+    return _dz_right(logp, yb, gb, V, 1.0, ge)     # dropped the 1/tau chain-rule factor
+
+
+def _dz_entropy_sign(logp, yb, gb, V, tau=1.0, ge=None):
+    return _dz_right(logp, yb, gb, V, tau, None if ge is None else -ge)   # wrong sign
+
+
+def _dz_entropy_no_h(logp, yb, gb, V, tau=1.0, ge=None):
+    p = np.exp(logp)
+    dz = -p * gb[:, None]
+    valid = (yb >= 0) & (yb < V)
+    r = np.nonzero(valid)[0]
+    dz[r, yb[r]] += gb[r]
+    if ge is not None:
+        dz -= ge[:, None] * p * logp               # dropped the + entropy term
+    return dz / tau
+
+
+def _sum_p_not_squared(p):
+    return p.sum(axis=1)
 
 
 PIN_SETS = {
@@ -59,6 +93,22 @@ PIN_SETS = {
         pins.test_backward_matches_central_differences,
         pins.test_backward_zero_hidden_closed_form,
         pins.test_grad_weight_column_sums,
+    ],
+    "temperature": [
+        lambda: pins.test_fp64_matches_brute_with_temperature(4, 24, 7, 0.7),
+        lambda: pins.test_one_hot_design_with_temperature(0.5),
+        pins.test_two_vocab_entries_softplus_with_temperature,
+        pins.test_high_temperature_limit_is_uniform,
+    ],
+    "backward_ext": [
+        pins.test_fp64_matches_brute_backward_temperature_and_entropy_grad,
+        lambda: pins.test_backward_with_temperature_and_entropy_matches_central_differences(0.6, False),
+        lambda: pins.test_backward_with_temperature_and_entropy_matches_central_differences(2.2, True),
+    ],
+    "sum_p2": [
+        lambda: pins.test_fp64_matches_brute_with_temperature(4, 24, 7, 0.7),
+        lambda: pins.test_one_hot_design_with_temperature(1.0),
+        pins.test_sum_p2_uniform_and_single_entry,
     ],
 }
 
@@ -78,6 +128,11 @@ def _some_pin_fails(kind):
     ("gather wrong index", "_gather_label", _gather_next, "forward"),
     ("dz sign", "_dz_block", _dz_sign, "backward"),
     ("dz without onehot", "_dz_block", _dz_no_onehot, "backward"),
+    ("temperature multiplies", "_block_softmax_terms", _terms_times_tau, "temperature"),
+    ("dz without 1/tau", "_dz_block", _dz_no_tau, "backward_ext"),
+    ("entropy gradient sign", "_dz_block", _dz_entropy_sign, "backward_ext"),
+    ("entropy gradient without the entropy term", "_dz_block", _dz_entropy_no_h, "backward_ext"),
+    ("sum_p2 not squared", "_sum_p2", _sum_p_not_squared, "sum_p2"),
 ])
 def test_pins_catch_planted_mistake(monkeypatch, name, target, mutant, kind):
     monkeypatch.setattr(fp64, target, mutant)
@@ -85,4 +140,4 @@ def test_pins_catch_planted_mistake(monkeypatch, name, target, mutant, kind):
 
 
 def test_unmutated_oracle_passes_all_pins():
-    assert not _some_pin_fails("forward") and not _some_pin_fails("backward")
+    assert not any(_some_pin_fails(kind) for kind in PIN_SETS)

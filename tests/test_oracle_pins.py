@@ -6,6 +6,7 @@ invariants, special cases and finite differences.  Each pin is chosen so that a 
 (a dropped term, a sign, an index, a transposed operand) breaks at least one of them.
 """
 import math
+import os
 
 import numpy as np
 import pytest
@@ -231,3 +232,148 @@ def test_grad_weight_column_sums():
     hf, gf = fp64.to_f64(h), fp64.to_f64(g)
     expect = -gf[3] * hf[3]
     np.testing.assert_allclose(gW.sum(axis=0), expect, atol=1e-12, rtol=0)
+
+
+# --------------------------------------------------------------------------------------------
+# temperature, sum of squared probabilities, entropy gradient
+# --------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,H,V,tau", [(4, 24, 7, 0.7), (3, 16, 5, 1.7), (2, 8, 1, 0.25)])
+def test_fp64_matches_brute_with_temperature(T, H, V, tau):
+    h, W, y = _rand_case(T, H, V, seed=21)
+    ref = fp64.forward(h, W, y, temperature=tau, sum_p2=True)
+    lp, ent, lse = brute.forward(h, W, y, temperature=tau)
+    p2 = brute.sum_p2(h, W, temperature=tau)
+    np.testing.assert_allclose(ref["logprob"], lp, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(ref["entropy"], ent, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(ref["lse"], lse, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(ref["sum_p2"], p2, rtol=0, atol=1e-12)
+
+
+def test_fp64_matches_brute_backward_temperature_and_entropy_grad():
+    T, H, V = 4, 12, 5
+    h, W, y = _rand_case(T, H, V, seed=22)
+    y = y.clone()
+    y[2] = -100
+    g = synth.upstream_grad(T, 22)
+    ge = synth.upstream_grad(T, 23)
+    for tau, gE in ((0.6, None), (1.0, ge), (1.3, ge)):
+        gh, gW = fp64.backward(h, W, y, g, temperature=tau, grad_entropy=gE)
+        bgh, bgW = brute.backward(h, W, y, g, temperature=tau, grad_entropy=gE)
+        np.testing.assert_allclose(gh, np.array(bgh), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(gW, np.array(bgW), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("tau", [0.5, 1.0, 2.5])
+def test_one_hot_design_with_temperature(tau):
+    # z_k = a at the hot index, 0 elsewhere, so z / tau is known exactly
+    V = H = 16
+    a = 3.5
+    W = torch.eye(V, dtype=torch.bfloat16)
+    ks = [0, 5, 15, 7]
+    h = torch.zeros((len(ks), H), dtype=torch.bfloat16)
+    for t, k in enumerate(ks):
+        h[t, k] = a
+    y = torch.tensor([0, 6, 15, 3], dtype=torch.int32)
+    out = fp64.forward(h, W, y, temperature=tau, sum_p2=True)
+    b = a / tau
+    S = math.exp(b) + V - 1
+    for t, k in enumerate(ks):
+        lp = (b if int(y[t]) == k else 0.0) - math.log(S)
+        ent = math.log(S) - b * math.exp(b) / S
+        p2 = (math.exp(2 * b) + V - 1) / S ** 2
+        assert abs(out["logprob"][t] - lp) < 1e-13
+        assert abs(out["entropy"][t] - ent) < 1e-13
+        assert abs(out["sum_p2"][t] - p2) < 1e-14
+        assert abs(out["lse"][t] - math.log(S)) < 1e-13
+
+
+def test_two_vocab_entries_softplus_with_temperature():
+    tau = 0.37
+    h, W, y = _rand_case(6, 8, 2, seed=24)
+    out = fp64.forward(h, W, y, temperature=tau, sum_p2=True)
+    z = fp64.to_f64(h) @ fp64.to_f64(W).T / tau
+    for t in range(6):
+        k = int(y[t])
+        d = z[t, 1 - k] - z[t, k]
+        lp = -(max(d, 0.0) + math.log1p(math.exp(-abs(d))))       # -softplus(d)
+        p = math.exp(lp)
+        assert abs(out["logprob"][t] - lp) < 1e-12
+        assert abs(out["sum_p2"][t] - (p * p + (1 - p) ** 2)) < 1e-12
+
+
+def test_high_temperature_limit_is_uniform():
+    V = 4096
+    h, W, y = _rand_case(3, 32, V, seed=25)
+    out = fp64.forward(h, W, y, temperature=1e12, sum_p2=True)   # |z| / tau ~ 1e-11
+    np.testing.assert_allclose(out["entropy"], math.log(V), rtol=0, atol=1e-9)
+    np.testing.assert_allclose(out["logprob"], -math.log(V), rtol=0, atol=1e-9)
+    np.testing.assert_allclose(out["sum_p2"], 1.0 / V, rtol=1e-9, atol=0)
+
+
+def test_sum_p2_uniform_and_single_entry():
+    out = fp64.forward(torch.zeros((2, 8), dtype=torch.bfloat16), synth.weight(1000, 8, 1, 1.0),
+                       torch.tensor([3, 999], dtype=torch.int32), sum_p2=True)
+    np.testing.assert_allclose(out["sum_p2"], 1e-3, rtol=1e-13, atol=0)
+    h, W, y = _rand_case(3, 8, 1, seed=26)
+    np.testing.assert_allclose(fp64.forward(h, W, y, sum_p2=True)["sum_p2"], 1.0, rtol=0, atol=1e-15)
+
+
+def _objective_full(h, W, y, g, tau, ge):
+    """sum_t g_t * (logprob_t, or -lse_t for an out-of-range label) + sum_t ge_t * entropy_t."""
+    out = fp64.forward(h, W, y, temperature=tau)
+    V = W.shape[0]
+    valid = (y >= 0) & (y < V)
+    f = np.sum(np.where(valid, g * out["logprob"], -g * out["lse"]))
+    if ge is not None:
+        f += np.sum(ge * out["entropy"])
+    return float(f)
+
+
+@pytest.mark.parametrize("tau,with_entropy", [(0.6, False), (1.0, True), (2.2, True)])
+def test_backward_with_temperature_and_entropy_matches_central_differences(tau, with_entropy):
+    T, H, V = 3, 5, 4
+    rng = np.random.default_rng(1)
+    h = rng.normal(size=(T, H))
+    W = rng.normal(size=(V, H)) * 0.7
+    y = np.array([1, -1, 3])
+    g = rng.normal(size=T)
+    ge = rng.normal(size=T) if with_entropy else None
+    gh, gW = fp64.backward(h, W, y, g, temperature=tau, grad_entropy=ge)
+    eps = 1e-6
+    for arr, grad in ((h, gh), (W, gW)):
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            old = arr[idx]
+            arr[idx] = old + eps
+            fp = _objective_full(h, W, y, g, tau, ge)
+            arr[idx] = old - eps
+            fm = _objective_full(h, W, y, g, tau, ge)
+            arr[idx] = old
+            num[idx] = (fp - fm) / (2 * eps)
+        np.testing.assert_allclose(grad, num, rtol=1e-6, atol=1e-8)
+
+
+def _golden_temperatures():
+    rows = []
+    with open(os.path.join(os.path.dirname(__file__), "golden", "bf16_temperatures.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                t, b = line.split()
+                rows.append((float(t), float(b)))
+    return rows
+
+
+def test_bf16_rounded_temperatures_printed_on_the_pages():
+    rows = _golden_temperatures()
+    assert len(rows) == 3
+    for t, b in rows:
+        assert torch.tensor(t, dtype=torch.float32).to(torch.bfloat16).item() == b
+    # the rounded temperature is a different input: on a random case it moves log-probs by more
+    # than the 2e-3 gate, so a path that rounded the temperature to bf16 would fail parity
+    h, W, y = _rand_case(64, 64, 512, seed=27, wstd=0.6)
+    for t, b in rows:
+        d = fp64.forward(h, W, y, temperature=float(np.float32(t)))["logprob"] - \
+            fp64.forward(h, W, y, temperature=b)["logprob"]
+        assert np.abs(d).max() > 2e-3
