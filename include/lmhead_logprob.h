@@ -73,7 +73,7 @@ typedef enum {
 } lmh_status_t;
 
 /* Bytes of workspace lmhead_logprob_fwd needs (also the stage entry points below).  Returns 0 for
- * invalid sizes.  The workspace holds one 16-byte record per (row, 128-column vocabulary chunk),
+ * invalid sizes.  The workspace holds one 20-byte record per (row, 128-column vocabulary chunk),
  * one float per row and 256 bytes of tile-scheduler counters; its initial contents do not matter.
  * Calls that may run concurrently need separate workspaces. */
 LMH_API size_t lmhead_logprob_fwd_workspace_size(int64_t T, int64_t H, int64_t V);
@@ -118,6 +118,62 @@ LMH_API lmh_status_t lmhead_logprob_bwd(const void* hidden, const void* weight, 
                                         const float* grad_logprob, const float* lse,
                                         float* grad_hidden, float* grad_weight, int accumulate_grad_weight,
                                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---- Extended entry points -------------------------------------------------------------------
+ *
+ * Temperature.  `temperature` (fp32, finite, > 0; otherwise LMH_ERR_INVALID_ARG) divides every
+ * fp32 logit before the softmax, so logprob, entropy, lse and sum_p2 are those of
+ * softmax(z / temperature), and the backward carries the chain-rule factor 1/temperature.  The
+ * division is an fp32 IEEE division of the fp32 logit by the caller's fp32 temperature — never
+ * by a bf16-rounded temperature (verl PR #8026 "batch-invariant actor forward and sampler
+ * log-prob formula", review on the temperature order: dividing bf16 logits by a temperature cast
+ * to bf16 changes every token; the sampler divides fp32 logits by the fp32 temperature).
+ * temperature == 1 gives exactly the bits of the plain entry points.
+ *
+ * sum_p2 [T] (or NULL): sum_j p_tj^2 of the same softmax, fp32 (verl PR #8026, first review:
+ * sum_pi_squared is computed next to the entropy from the same logits).
+ *
+ * Entropy gradient: grad_entropy [T] (or NULL) is the upstream gradient of the entropies; the
+ * logit gradient then also carries -grad_entropy_t * p_tj * (log p_tj + entropy_t), with
+ * entropy [T] the forward's entropy output for the same inputs and temperature (required when
+ * grad_entropy is given).  The pages leave this gradient unwired (SkyRL PR #1765 "[megatron]
+ * Triton backend for fused LM-head log-prob", PR summary); it is the derivative of the entropy
+ * definition above.
+ */
+LMH_API lmh_status_t lmhead_logprob_fwd_ex(const void* hidden, const void* weight, const int32_t* labels,
+                                           int64_t T, int64_t H, int64_t V, float temperature,
+                                           float* logprob, float* entropy, float* lse, float* sum_p2,
+                                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Partials stage over one vocabulary shard.  The weight rows given (`weight` [V,H]) are the
+ * vocabulary ids [vocab_start, vocab_start + V) of a vocabulary of vocab_total ids; the
+ * workspace is sized for vocab_total (lmhead_logprob_fwd_workspace_size(T, H, vocab_total)) and
+ * this call writes the records of its own 128-row chunks only, plus the label logit of every row
+ * whose label falls in its rows.  Running the shards of a vocabulary in any order into one
+ * workspace, then lmhead_logprob_fwd_finalize_ex with vocab_total, gives the bits of one call on
+ * the whole weight.  A tensor-parallel caller exchanges the record rows of its shard instead (the
+ * vocabulary-sharded layout of SkyRL PR #1765: each rank holds a slice of the LM head and only
+ * the owner of a label contributes its logit).  Requirements: vocab_start a multiple of 128;
+ * vocab_start + V <= vocab_total (LMH_ERR_INVALID_ARG otherwise); V a multiple of 128 unless the
+ * shard ends at vocab_total (LMH_ERR_UNSUPPORTED otherwise).  want_sum_p2 (0 or 1) records what
+ * sum_p2 needs; finalize may only be asked for sum_p2 if every shard was run with it. */
+LMH_API lmh_status_t lmhead_logprob_fwd_partials_ex(const void* hidden, const void* weight, const int32_t* labels,
+                                                    int64_t T, int64_t H, int64_t V, float temperature,
+                                                    int64_t vocab_start, int64_t vocab_total, int want_sum_p2,
+                                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+LMH_API lmh_status_t lmhead_logprob_fwd_finalize_ex(const int32_t* labels, int64_t T, int64_t H, int64_t V,
+                                                    float* logprob, float* entropy, float* lse, float* sum_p2,
+                                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Backward with a temperature and an optional entropy gradient (see above); lse is the one the
+ * forward wrote with the same temperature.  grad_logprob is required (pass zeros when only the
+ * entropy carries a gradient). */
+LMH_API lmh_status_t lmhead_logprob_bwd_ex(const void* hidden, const void* weight, const int32_t* labels,
+                                           int64_t T, int64_t H, int64_t V, float temperature,
+                                           const float* grad_logprob, const float* lse,
+                                           const float* grad_entropy, const float* entropy,
+                                           float* grad_hidden, float* grad_weight, int accumulate_grad_weight,
+                                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Static English text for a status code (never NULL). */
 LMH_API const char* lmhead_status_string(lmh_status_t s);

@@ -28,14 +28,20 @@ LMH_ERR_HIP = 4
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
 _SZ = ctypes.c_size_t
+_F = ctypes.c_float
+_INT = ctypes.c_int
 _SIGNATURES = {
     "lmhead_logprob_fwd_workspace_size": (_SZ, [_I64, _I64, _I64]),
-    "lmhead_logprob_fwd": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P]),
-    "lmhead_logprob_fwd_partials": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P]),
-    "lmhead_logprob_fwd_finalize": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P]),
+    "lmhead_logprob_fwd": (_INT, [_P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P]),
+    "lmhead_logprob_fwd_partials": (_INT, [_P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P]),
+    "lmhead_logprob_fwd_finalize": (_INT, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P]),
     "lmhead_logprob_bwd_workspace_size": (_SZ, [_I64, _I64, _I64]),
-    "lmhead_logprob_bwd": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, ctypes.c_int, _P, _SZ, _P]),
-    "lmhead_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "lmhead_logprob_bwd": (_INT, [_P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _INT, _P, _SZ, _P]),
+    "lmhead_logprob_fwd_ex": (_INT, [_P, _P, _P, _I64, _I64, _I64, _F, _P, _P, _P, _P, _P, _SZ, _P]),
+    "lmhead_logprob_fwd_partials_ex": (_INT, [_P, _P, _P, _I64, _I64, _I64, _F, _I64, _I64, _INT, _P, _SZ, _P]),
+    "lmhead_logprob_fwd_finalize_ex": (_INT, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _SZ, _P]),
+    "lmhead_logprob_bwd_ex": (_INT, [_P, _P, _P, _I64, _I64, _I64, _F, _P, _P, _P, _P, _P, _P, _INT, _P, _SZ, _P]),
+    "lmhead_status_string": (ctypes.c_char_p, [_INT]),
 }
 
 _lib = None
@@ -162,6 +168,62 @@ def lmhead_logprob_bwd(hidden, weight, labels, grad_logprob, lse, grad_hidden=No
                                     _ptr(workspace), ws_bytes, _stream(stream)), "lmhead_logprob_bwd")
 
 
+def _nbytes(workspace) -> int:
+    return 0 if workspace is None else workspace.numel() * workspace.element_size()
+
+
+def lmhead_logprob_fwd_ex(hidden, weight, labels, temperature: float, logprob, entropy=None, lse=None, sum_p2=None,
+                          workspace=None, stream=None) -> None:
+    T, H, V = _dims(hidden, weight)
+    _check_tensor(hidden, "hidden", torch.bfloat16)
+    _check_tensor(weight, "weight", torch.bfloat16)
+    _check_tensor(labels, "labels", torch.int32, T)
+    for t, n in ((logprob, "logprob"), (entropy, "entropy"), (lse, "lse"), (sum_p2, "sum_p2")):
+        _check_tensor(t, n, torch.float32, T)
+    _check(lib().lmhead_logprob_fwd_ex(_ptr(hidden), _ptr(weight), _ptr(labels), T, H, V, float(temperature),
+                                       _ptr(logprob), _ptr(entropy), _ptr(lse), _ptr(sum_p2), _ptr(workspace),
+                                       _nbytes(workspace), _stream(stream)), "lmhead_logprob_fwd_ex")
+
+
+def lmhead_logprob_fwd_partials_ex(hidden, weight, labels, temperature: float, vocab_start: int, vocab_total: int,
+                                   want_sum_p2: bool, workspace, stream=None) -> None:
+    T, H, V = _dims(hidden, weight)
+    _check_tensor(hidden, "hidden", torch.bfloat16)
+    _check_tensor(weight, "weight", torch.bfloat16)
+    _check_tensor(labels, "labels", torch.int32, T)
+    _check(lib().lmhead_logprob_fwd_partials_ex(_ptr(hidden), _ptr(weight), _ptr(labels), T, H, V, float(temperature),
+                                                int(vocab_start), int(vocab_total), int(bool(want_sum_p2)),
+                                                _ptr(workspace), _nbytes(workspace), _stream(stream)),
+           "lmhead_logprob_fwd_partials_ex")
+
+
+def lmhead_logprob_fwd_finalize_ex(labels, T, H, V, logprob, entropy=None, lse=None, sum_p2=None, workspace=None,
+                                   stream=None) -> None:
+    _check_tensor(labels, "labels", torch.int32, T)
+    for t, n in ((logprob, "logprob"), (entropy, "entropy"), (lse, "lse"), (sum_p2, "sum_p2")):
+        _check_tensor(t, n, torch.float32, T)
+    _check(lib().lmhead_logprob_fwd_finalize_ex(_ptr(labels), T, H, V, _ptr(logprob), _ptr(entropy), _ptr(lse),
+                                                _ptr(sum_p2), _ptr(workspace), _nbytes(workspace), _stream(stream)),
+           "lmhead_logprob_fwd_finalize_ex")
+
+
+def lmhead_logprob_bwd_ex(hidden, weight, labels, temperature: float, grad_logprob, lse, grad_entropy=None,
+                          entropy=None, grad_hidden=None, grad_weight=None, accumulate_grad_weight: bool = False,
+                          workspace=None, stream=None) -> None:
+    T, H, V = _dims(hidden, weight)
+    _check_tensor(hidden, "hidden", torch.bfloat16)
+    _check_tensor(weight, "weight", torch.bfloat16)
+    _check_tensor(labels, "labels", torch.int32, T)
+    for t, n in ((grad_logprob, "grad_logprob"), (lse, "lse"), (grad_entropy, "grad_entropy"), (entropy, "entropy")):
+        _check_tensor(t, n, torch.float32, T)
+    _check_tensor(grad_hidden, "grad_hidden", torch.float32, T * H)
+    _check_tensor(grad_weight, "grad_weight", torch.float32, V * H)
+    _check(lib().lmhead_logprob_bwd_ex(_ptr(hidden), _ptr(weight), _ptr(labels), T, H, V, float(temperature),
+                                       _ptr(grad_logprob), _ptr(lse), _ptr(grad_entropy), _ptr(entropy),
+                                       _ptr(grad_hidden), _ptr(grad_weight), int(bool(accumulate_grad_weight)),
+                                       _ptr(workspace), _nbytes(workspace), _stream(stream)), "lmhead_logprob_bwd_ex")
+
+
 # ---------------------------------------------------------------------------------------------
 # allocation helpers and the autograd wrapper
 # ---------------------------------------------------------------------------------------------
@@ -172,62 +234,80 @@ def _workspace(nbytes: int, device) -> torch.Tensor:
 
 
 def forward(hidden: torch.Tensor, weight: torch.Tensor, labels: torch.Tensor, entropy: bool = False,
-            want_lse: bool = False, stream=None):
-    """Allocate outputs and workspace with torch and run lmhead_logprob_fwd.
+            want_lse: bool = False, stream=None, temperature: float = 1.0, sum_p2: bool = False):
+    """Allocate outputs and workspace with torch and run lmhead_logprob_fwd (lmhead_logprob_fwd_ex
+    when a temperature or sum_p2 is asked for).
 
-    Returns (logprob [T] fp32, entropy [T] fp32 or None, lse [T] fp32 or None)."""
+    Returns (logprob [T] fp32, entropy [T] fp32 or None, lse [T] fp32 or None), plus sum_p2 [T]
+    as a fourth element when sum_p2 is true."""
     T, H, V = _dims(hidden, weight)
     dev = hidden.device
     lp = torch.empty(T, dtype=torch.float32, device=dev)
     ent = torch.empty(T, dtype=torch.float32, device=dev) if entropy else None
     lse = torch.empty(T, dtype=torch.float32, device=dev) if want_lse else None
+    p2 = torch.empty(T, dtype=torch.float32, device=dev) if sum_p2 else None
     ws = _workspace(lmhead_logprob_fwd_workspace_size(T, H, V), dev)
-    lmhead_logprob_fwd(hidden, weight, labels, lp, ent, lse, ws, stream)
-    return lp, ent, lse
+    if temperature == 1.0 and not sum_p2:
+        lmhead_logprob_fwd(hidden, weight, labels, lp, ent, lse, ws, stream)
+    else:
+        lmhead_logprob_fwd_ex(hidden, weight, labels, temperature, lp, ent, lse, p2, ws, stream)
+    return (lp, ent, lse, p2) if sum_p2 else (lp, ent, lse)
 
 
-def backward(hidden, weight, labels, grad_logprob, lse, need_hidden=True, need_weight=True, stream=None):
-    """Allocate gradients and workspace with torch and run lmhead_logprob_bwd (overwrite mode)."""
+def backward(hidden, weight, labels, grad_logprob, lse, need_hidden=True, need_weight=True, stream=None,
+             temperature: float = 1.0, grad_entropy=None, entropy=None):
+    """Allocate gradients and workspace with torch and run lmhead_logprob_bwd (overwrite mode;
+    lmhead_logprob_bwd_ex when a temperature or an entropy gradient is given)."""
     T, H, V = _dims(hidden, weight)
     dev = hidden.device
     gh = torch.empty((T, H), dtype=torch.float32, device=dev) if need_hidden else None
     gw = torch.empty((V, H), dtype=torch.float32, device=dev) if need_weight else None
     ws = _workspace(lmhead_logprob_bwd_workspace_size(T, H, V), dev)
-    lmhead_logprob_bwd(hidden, weight, labels, grad_logprob, lse, gh, gw, False, ws, stream)
+    if temperature == 1.0 and grad_entropy is None:
+        lmhead_logprob_bwd(hidden, weight, labels, grad_logprob, lse, gh, gw, False, ws, stream)
+    else:
+        lmhead_logprob_bwd_ex(hidden, weight, labels, temperature, grad_logprob, lse, grad_entropy, entropy, gh, gw,
+                              False, ws, stream)
     return gh, gw
 
 
 class _FusedLogprob(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, hidden, weight, labels, want_entropy):
-        lp, ent, lse = forward(hidden, weight, labels, entropy=want_entropy, want_lse=True)
-        ctx.save_for_backward(hidden, weight, labels, lse)
-        if ent is not None:
-            ctx.mark_non_differentiable(ent)
+    def forward(ctx, hidden, weight, labels, want_entropy, temperature):
+        lp, ent, lse = forward(hidden, weight, labels, entropy=want_entropy, want_lse=True, temperature=temperature)
+        ctx.save_for_backward(hidden, weight, labels, lse, ent)
+        ctx.temperature = temperature
+        ctx.set_materialize_grads(False)
         return lp, ent
 
     @staticmethod
     def backward(ctx, grad_lp, grad_ent):
-        hidden, weight, labels, lse = ctx.saved_tensors
-        if grad_ent is not None and bool(torch.any(grad_ent != 0)):
-            raise RuntimeError("entropy has no gradient in the fused LM-head log-prob")
-        g = grad_lp.contiguous().to(torch.float32)
-        gh, gw = backward(hidden, weight, labels, g, lse, ctx.needs_input_grad[0], ctx.needs_input_grad[1])
-        return gh, gw, None, None
+        hidden, weight, labels, lse, ent = ctx.saved_tensors
+        T = hidden.shape[0]
+        if grad_lp is None:
+            g = torch.zeros(T, dtype=torch.float32, device=hidden.device)
+        else:
+            g = grad_lp.contiguous().to(torch.float32)
+        ge = None if grad_ent is None else grad_ent.contiguous().to(torch.float32)
+        gh, gw = backward(hidden, weight, labels, g, lse, ctx.needs_input_grad[0], ctx.needs_input_grad[1],
+                          temperature=ctx.temperature, grad_entropy=ge, entropy=ent if ge is not None else None)
+        return gh, gw, None, None, None
 
 
-def logprob(hidden: torch.Tensor, weight: torch.Tensor, labels: torch.Tensor, entropy: bool = False):
+def logprob(hidden: torch.Tensor, weight: torch.Tensor, labels: torch.Tensor, entropy: bool = False,
+            temperature: float = 1.0):
     """Fused LM-head log-prob with autograd.
 
     hidden [..., H] (any float dtype; cast to weight's dtype before the projection, and the
     gradient cast back, as the pages' adapter does), weight [V, H] bf16, labels [...] integer.
-    Leading dimensions are flattened to token rows.  Returns (logprob [...], entropy [...] or
-    None), fp32; entropy carries no gradient."""
+    Leading dimensions are flattened to token rows.  The logits are divided by the fp32
+    temperature before the softmax.  Returns (logprob [...], entropy [...] or None), fp32; both
+    are differentiable (the entropy's gradient is -p (log p + entropy) per logit)."""
     if weight.dtype != torch.bfloat16:
         raise ValueError("weight must be bf16")
     lead = hidden.shape[:-1]
     h2 = hidden.reshape(-1, hidden.shape[-1])
     h2 = h2.to(weight.dtype).contiguous()   # differentiable: grad_hidden is cast back by autograd
     y = labels.reshape(-1).to(torch.int32).contiguous()
-    lp, ent = _FusedLogprob.apply(h2, weight.contiguous(), y, entropy)
+    lp, ent = _FusedLogprob.apply(h2, weight.contiguous(), y, entropy, float(temperature))
     return lp.reshape(lead), (ent.reshape(lead) if ent is not None else None)

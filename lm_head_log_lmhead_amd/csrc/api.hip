@@ -2,6 +2,8 @@
 // launch.  Every check runs before the first launch; a failed check launches nothing.
 #include "lmhead_logprob.h"
 
+#include <math.h>
+
 #include "kernels.hpp"
 
 namespace {
@@ -28,14 +30,17 @@ lmh_status_t check_sizes(int64_t T, int64_t H, int64_t V) {
 }
 
 struct FwdWs {
-  size_t rec_off, zy_off, sched_off, total;
+  size_t rec_off, rec2_off, zy_off, sched_off, total;
 };
 
+// Forward workspace for a vocabulary of V rows: records and squared-sum records for every
+// 128-row chunk, label logits, tile counters.
 FwdWs fwd_ws(int64_t T, int64_t V) {
   const int64_t n_c = (V + lmh::VOCAB_CHUNK - 1) / lmh::VOCAB_CHUNK;
   FwdWs w;
   w.rec_off = 0;
-  w.zy_off = align256((size_t)n_c * (size_t)T * 16);
+  w.rec2_off = align256((size_t)n_c * (size_t)T * 16);
+  w.zy_off = w.rec2_off + align256((size_t)n_c * (size_t)T * 4);
   w.sched_off = w.zy_off + align256((size_t)T * 4);
   w.total = w.sched_off + align256(lmh::SCHED_WORDS * sizeof(int));
   return w;
@@ -59,9 +64,16 @@ lmh_status_t check_out(const float* p, bool required) {
   return aligned(p, 4) ? LMH_OK : LMH_ERR_UNSUPPORTED;
 }
 
+lmh_status_t check_in(const float* p) {
+  if (!p) return LMH_ERR_INVALID_ARG;
+  return aligned(p, 4) ? LMH_OK : LMH_ERR_UNSUPPORTED;
+}
+
+lmh_status_t check_temperature(float t) { return (isfinite(t) && t > 0.0f) ? LMH_OK : LMH_ERR_INVALID_ARG; }
+
 lmh_status_t launched() { return hipGetLastError() == hipSuccess ? LMH_OK : LMH_ERR_HIP; }
 
-// Compute units of the current device (the large-T forward grid has one workgroup per CU).
+// Compute units of the current device (the large-T grids have one workgroup per CU).
 lmh_status_t device_cus(int& cus) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return LMH_ERR_HIP;
@@ -71,8 +83,9 @@ lmh_status_t device_cus(int& cus) {
 }
 
 FwdArgs make_fwd_args(const void* hidden, const void* weight, const int32_t* labels, int64_t T, int64_t H,
-                      int64_t V, float* logprob, float* entropy, float* lse, void* workspace) {
-  const FwdWs w = fwd_ws(T, V);
+                      int64_t V, int64_t vocab_start, int64_t vocab_total, float temperature, int want_p2,
+                      float* logprob, float* entropy, float* lse, float* sum_p2, void* workspace) {
+  const FwdWs w = fwd_ws(T, vocab_total);
   char* ws = static_cast<char*>(workspace);
   FwdArgs a;
   a.hidden = static_cast<const __bf16*>(hidden);
@@ -81,12 +94,18 @@ FwdArgs make_fwd_args(const void* hidden, const void* weight, const int32_t* lab
   a.T = (int)T;
   a.H = (int)H;
   a.V = (int)V;
+  a.vocab_start = (int)vocab_start;
+  a.vocab_total = (int)vocab_total;
+  a.temperature = temperature;
+  a.want_p2 = want_p2;
   a.rec = reinterpret_cast<lmh::f32x4*>(ws + w.rec_off);
+  a.rec2 = reinterpret_cast<float*>(ws + w.rec2_off);
   a.zy = reinterpret_cast<float*>(ws + w.zy_off);
   a.sched = reinterpret_cast<int*>(ws + w.sched_off);
   a.logprob = logprob;
   a.entropy = entropy;
   a.lse = lse;
+  a.sum_p2 = sum_p2;
   a.cus = 0;
   return a;
 }
@@ -97,32 +116,38 @@ FwdArgs make_fwd_args(const void* hidden, const void* weight, const int32_t* lab
     if (s_ != LMH_OK) return s_;           \
   } while (0)
 
-}  // namespace
-
-extern "C" {
-
-size_t lmhead_logprob_fwd_workspace_size(int64_t T, int64_t H, int64_t V) {
-  if (check_sizes(T, H, V) != LMH_OK) return 0;
-  return fwd_ws(T, V).total;
+// The weight rows of a call are the vocabulary ids [vocab_start, vocab_start + V) of a
+// vocabulary of vocab_total; shards start on a chunk and all but the last cover whole chunks.
+lmh_status_t check_shard(int64_t H, int64_t V, int64_t vocab_start, int64_t vocab_total) {
+  if (V <= 0 || vocab_start < 0 || vocab_total <= 0) return LMH_ERR_INVALID_ARG;
+  if (vocab_start + V > vocab_total) return LMH_ERR_INVALID_ARG;
+  if (vocab_start % lmh::VOCAB_CHUNK != 0) return LMH_ERR_UNSUPPORTED;
+  if (V % lmh::VOCAB_CHUNK != 0 && vocab_start + V != vocab_total) return LMH_ERR_UNSUPPORTED;
+  (void)H;
+  return LMH_OK;
 }
 
-lmh_status_t lmhead_logprob_fwd_partials(const void* hidden, const void* weight, const int32_t* labels, int64_t T,
-                                         int64_t H, int64_t V, void* workspace, size_t workspace_bytes,
-                                         hipStream_t stream) {
-  LMH_TRY(check_sizes(T, H, V));
+lmh_status_t fwd_partials_impl(const void* hidden, const void* weight, const int32_t* labels, int64_t T, int64_t H,
+                               int64_t V, float temperature, int64_t vocab_start, int64_t vocab_total,
+                               int want_sum_p2, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  LMH_TRY(check_sizes(T, H, vocab_total));
+  LMH_TRY(check_shard(H, V, vocab_start, vocab_total));
+  if (want_sum_p2 != 0 && want_sum_p2 != 1) return LMH_ERR_INVALID_ARG;
+  LMH_TRY(check_temperature(temperature));
   if (T == 0) return LMH_OK;
   LMH_TRY(check_inputs(hidden, weight, labels));
-  LMH_TRY(check_ws(workspace, workspace_bytes, fwd_ws(T, V).total));
-  FwdArgs a = make_fwd_args(hidden, weight, labels, T, H, V, nullptr, nullptr, nullptr, workspace);
+  LMH_TRY(check_ws(workspace, workspace_bytes, fwd_ws(T, vocab_total).total));
+  FwdArgs a = make_fwd_args(hidden, weight, labels, T, H, V, vocab_start, vocab_total, temperature, want_sum_p2,
+                            nullptr, nullptr, nullptr, nullptr, workspace);
   LMH_TRY(device_cus(a.cus));
   (void)hipGetLastError();  // clear any stale error so the check after launching sees only ours
   lmh::launch_fwd_partials(a, stream);
   return launched();
 }
 
-lmh_status_t lmhead_logprob_fwd_finalize(const int32_t* labels, int64_t T, int64_t H, int64_t V, float* logprob,
-                                         float* entropy, float* lse, void* workspace, size_t workspace_bytes,
-                                         hipStream_t stream) {
+lmh_status_t fwd_finalize_impl(const int32_t* labels, int64_t T, int64_t H, int64_t V, float* logprob,
+                               float* entropy, float* lse, float* sum_p2, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
   LMH_TRY(check_sizes(T, H, V));
   if (T == 0) return LMH_OK;
   if (!labels) return LMH_ERR_INVALID_ARG;
@@ -130,24 +155,30 @@ lmh_status_t lmhead_logprob_fwd_finalize(const int32_t* labels, int64_t T, int64
   LMH_TRY(check_out(logprob, true));
   LMH_TRY(check_out(entropy, false));
   LMH_TRY(check_out(lse, false));
+  LMH_TRY(check_out(sum_p2, false));
   LMH_TRY(check_ws(workspace, workspace_bytes, fwd_ws(T, V).total));
   (void)hipGetLastError();
-  lmh::launch_fwd_finalize(make_fwd_args(nullptr, nullptr, labels, T, H, V, logprob, entropy, lse, workspace),
-                           stream);
+  lmh::launch_fwd_finalize(
+      make_fwd_args(nullptr, nullptr, labels, T, H, V, 0, V, 1.0f, sum_p2 != nullptr, logprob, entropy, lse, sum_p2,
+                    workspace),
+      stream);
   return launched();
 }
 
-lmh_status_t lmhead_logprob_fwd(const void* hidden, const void* weight, const int32_t* labels, int64_t T, int64_t H,
-                                int64_t V, float* logprob, float* entropy, float* lse, void* workspace,
-                                size_t workspace_bytes, hipStream_t stream) {
+lmh_status_t fwd_impl(const void* hidden, const void* weight, const int32_t* labels, int64_t T, int64_t H, int64_t V,
+                      float temperature, float* logprob, float* entropy, float* lse, float* sum_p2, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
   LMH_TRY(check_sizes(T, H, V));
+  LMH_TRY(check_temperature(temperature));
   if (T == 0) return LMH_OK;
   LMH_TRY(check_inputs(hidden, weight, labels));
   LMH_TRY(check_out(logprob, true));
   LMH_TRY(check_out(entropy, false));
   LMH_TRY(check_out(lse, false));
+  LMH_TRY(check_out(sum_p2, false));
   LMH_TRY(check_ws(workspace, workspace_bytes, fwd_ws(T, V).total));
-  FwdArgs a = make_fwd_args(hidden, weight, labels, T, H, V, logprob, entropy, lse, workspace);
+  FwdArgs a = make_fwd_args(hidden, weight, labels, T, H, V, 0, V, temperature, sum_p2 != nullptr, logprob, entropy,
+                            lse, sum_p2, workspace);
   LMH_TRY(device_cus(a.cus));
   (void)hipGetLastError();
   lmh::launch_fwd_partials(a, stream);
@@ -156,22 +187,22 @@ lmh_status_t lmhead_logprob_fwd(const void* hidden, const void* weight, const in
   return launched();
 }
 
-size_t lmhead_logprob_bwd_workspace_size(int64_t T, int64_t H, int64_t V) {
-  if (check_sizes(T, H, V) != LMH_OK) return 0;
-  return lmh::bwd_layout(T, H, V).total;
-}
-
-lmh_status_t lmhead_logprob_bwd(const void* hidden, const void* weight, const int32_t* labels, int64_t T, int64_t H,
-                                int64_t V, const float* grad_logprob, const float* lse, float* grad_hidden,
-                                float* grad_weight, int accumulate_grad_weight, void* workspace,
-                                size_t workspace_bytes, hipStream_t stream) {
+lmh_status_t bwd_impl(const void* hidden, const void* weight, const int32_t* labels, int64_t T, int64_t H, int64_t V,
+                      float temperature, const float* grad_logprob, const float* lse, const float* grad_entropy,
+                      const float* entropy, float* grad_hidden, float* grad_weight, int accumulate_grad_weight,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
   LMH_TRY(check_sizes(T, H, V));
   if (accumulate_grad_weight != 0 && accumulate_grad_weight != 1) return LMH_ERR_INVALID_ARG;
+  LMH_TRY(check_temperature(temperature));
   if (T >= MAX_T_BWD) return LMH_ERR_UNSUPPORTED;
   if (T == 0) return LMH_OK;  // no rows: nothing is launched and the gradient buffers are untouched
   LMH_TRY(check_inputs(hidden, weight, labels));
-  if (!grad_logprob || !lse) return LMH_ERR_INVALID_ARG;
-  if (!aligned(grad_logprob, 4) || !aligned(lse, 4)) return LMH_ERR_UNSUPPORTED;
+  LMH_TRY(check_in(grad_logprob));
+  LMH_TRY(check_in(lse));
+  if (grad_entropy) {
+    LMH_TRY(check_in(grad_entropy));
+    LMH_TRY(check_in(entropy));
+  }
   LMH_TRY(check_out(grad_hidden, false));
   LMH_TRY(check_out(grad_weight, false));
   const lmh::BwdLayout L = lmh::bwd_layout(T, H, V);
@@ -185,6 +216,9 @@ lmh_status_t lmhead_logprob_bwd(const void* hidden, const void* weight, const in
   a.labels = labels;
   a.grad = grad_logprob;
   a.lse = lse;
+  a.grad_entropy = grad_entropy;
+  a.entropy = grad_entropy ? entropy : nullptr;
+  a.temperature = temperature;
   a.grad_hidden = grad_hidden;
   a.grad_weight = grad_weight;
   a.accumulate_gw = accumulate_grad_weight;
@@ -194,11 +228,83 @@ lmh_status_t lmhead_logprob_bwd(const void* hidden, const void* weight, const in
   return launched();
 }
 
+}  // namespace
+
+extern "C" {
+
+size_t lmhead_logprob_fwd_workspace_size(int64_t T, int64_t H, int64_t V) {
+  if (check_sizes(T, H, V) != LMH_OK) return 0;
+  return fwd_ws(T, V).total;
+}
+
+lmh_status_t lmhead_logprob_fwd_partials(const void* hidden, const void* weight, const int32_t* labels, int64_t T,
+                                         int64_t H, int64_t V, void* workspace, size_t workspace_bytes,
+                                         hipStream_t stream) {
+  return fwd_partials_impl(hidden, weight, labels, T, H, V, 1.0f, 0, V, 0, workspace, workspace_bytes, stream);
+}
+
+lmh_status_t lmhead_logprob_fwd_partials_ex(const void* hidden, const void* weight, const int32_t* labels, int64_t T,
+                                            int64_t H, int64_t V, float temperature, int64_t vocab_start,
+                                            int64_t vocab_total, int want_sum_p2, void* workspace,
+                                            size_t workspace_bytes, hipStream_t stream) {
+  return fwd_partials_impl(hidden, weight, labels, T, H, V, temperature, vocab_start, vocab_total, want_sum_p2,
+                           workspace, workspace_bytes, stream);
+}
+
+lmh_status_t lmhead_logprob_fwd_finalize(const int32_t* labels, int64_t T, int64_t H, int64_t V, float* logprob,
+                                         float* entropy, float* lse, void* workspace, size_t workspace_bytes,
+                                         hipStream_t stream) {
+  return fwd_finalize_impl(labels, T, H, V, logprob, entropy, lse, nullptr, workspace, workspace_bytes, stream);
+}
+
+lmh_status_t lmhead_logprob_fwd_finalize_ex(const int32_t* labels, int64_t T, int64_t H, int64_t V, float* logprob,
+                                            float* entropy, float* lse, float* sum_p2, void* workspace,
+                                            size_t workspace_bytes, hipStream_t stream) {
+  return fwd_finalize_impl(labels, T, H, V, logprob, entropy, lse, sum_p2, workspace, workspace_bytes, stream);
+}
+
+lmh_status_t lmhead_logprob_fwd(const void* hidden, const void* weight, const int32_t* labels, int64_t T, int64_t H,
+                                int64_t V, float* logprob, float* entropy, float* lse, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  return fwd_impl(hidden, weight, labels, T, H, V, 1.0f, logprob, entropy, lse, nullptr, workspace, workspace_bytes,
+                  stream);
+}
+
+lmh_status_t lmhead_logprob_fwd_ex(const void* hidden, const void* weight, const int32_t* labels, int64_t T,
+                                   int64_t H, int64_t V, float temperature, float* logprob, float* entropy,
+                                   float* lse, float* sum_p2, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream) {
+  return fwd_impl(hidden, weight, labels, T, H, V, temperature, logprob, entropy, lse, sum_p2, workspace,
+                  workspace_bytes, stream);
+}
+
+size_t lmhead_logprob_bwd_workspace_size(int64_t T, int64_t H, int64_t V) {
+  if (check_sizes(T, H, V) != LMH_OK) return 0;
+  return lmh::bwd_layout(T, H, V).total;
+}
+
+lmh_status_t lmhead_logprob_bwd(const void* hidden, const void* weight, const int32_t* labels, int64_t T, int64_t H,
+                                int64_t V, const float* grad_logprob, const float* lse, float* grad_hidden,
+                                float* grad_weight, int accumulate_grad_weight, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  return bwd_impl(hidden, weight, labels, T, H, V, 1.0f, grad_logprob, lse, nullptr, nullptr, grad_hidden,
+                  grad_weight, accumulate_grad_weight, workspace, workspace_bytes, stream);
+}
+
+lmh_status_t lmhead_logprob_bwd_ex(const void* hidden, const void* weight, const int32_t* labels, int64_t T,
+                                   int64_t H, int64_t V, float temperature, const float* grad_logprob,
+                                   const float* lse, const float* grad_entropy, const float* entropy,
+                                   float* grad_hidden, float* grad_weight, int accumulate_grad_weight,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return bwd_impl(hidden, weight, labels, T, H, V, temperature, grad_logprob, lse, grad_entropy, entropy, grad_hidden,
+                  grad_weight, accumulate_grad_weight, workspace, workspace_bytes, stream);
+}
+
 const char* lmhead_status_string(lmh_status_t s) {
   switch (s) {
     case LMH_OK: return "ok";
-    case LMH_ERR_INVALID_ARG: return "invalid argument (null required pointer or non-positive size)";
-    case LMH_ERR_UNSUPPORTED: return "unsupported (H % 8 != 0, a size limit, or a misaligned pointer)";
+    case LMH_ERR_INVALID_ARG: return "invalid argument (null required pointer, non-positive size or temperature)";
+    case LMH_ERR_UNSUPPORTED: return "unsupported (H % 8 != 0, a size limit, a misaligned pointer or shard)";
     case LMH_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case LMH_ERR_HIP: return "HIP launch error";
   }

@@ -24,14 +24,20 @@ namespace lmh {
 // K3: dz tiles
 // ---------------------------------------------------------------------------------------------
 
-constexpr int DZ_PITCH = WAVE_M * 2 + 16;
-constexpr int BWD_SCHED_WORDS = 16;        // tile counters per vocabulary step (one per XCD)  // bytes per staged token row (padded against conflicts)
+constexpr int DZ_PITCH = WAVE_M * 2 + 16;  // bytes per staged token row (padded against conflicts)
+constexpr int BWD_SCHED_WORDS = 16;        // tile counters per vocabulary step (one per XCD)
 
-template <class Cfg>
+// With a temperature tau the logits are z / tau and the logit gradient carries 1/tau; with an
+// entropy gradient gE the term -gE p (log p + H) is added (log p = z / tau - lse), as in the
+// forward definition (verl PR #8026 review on the temperature order; the entropy gradient that
+// SkyRL PR #1765 leaves unwired).
+template <class Cfg, bool SCALED, bool EGRAD>
 __global__ __launch_bounds__(Cfg::NTHREADS) void bwd_dz_kernel(
     const __bf16* __restrict__ hidden, const __bf16* __restrict__ weight, const int* __restrict__ labels,
-    const float* __restrict__ grad, const float* __restrict__ lse, int T, int H, int V, int vs0, int Vc,
-    int Vs, int n_mt, int n_nt, __bf16* __restrict__ dz) {
+    const float* __restrict__ grad, const float* __restrict__ lse, const float* __restrict__ grad_entropy,
+    const float* __restrict__ entropy, float temperature, int T, int H, int V, int vs0, int Vc, int Vs, int n_mt,
+    int n_nt, __bf16* __restrict__ dz) {
+  loop_placement_pad<4 + 2 * SCALED + EGRAD>();
   constexpr int STAGE_OUT = Cfg::NWAVES * Cfg::WAVE_N * DZ_PITCH;
   constexpr int LDS = PingPong<Cfg>::LDS_BYTES > STAGE_OUT ? PingPong<Cfg>::LDS_BYTES : STAGE_OUT;
   __shared__ __attribute__((aligned(1024))) char lds[LDS];
@@ -62,19 +68,31 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void bwd_dz_kernel(
   for (int n = 0; n < Cfg::NSUB; ++n) {
     const int tok = tok0 + n * MFMA_MN + j;
     const bool tok_ok = tok < T;
-    const float g = tok_ok ? grad[tok] : 0.f;
+    float g = tok_ok ? grad[tok] : 0.f;
     const float L = tok_ok ? lse[tok] : 0.f;
     const int y = tok_ok ? labels[tok] : -1;
+    float ge = 0.f, He = 0.f;
+    if (EGRAD) {
+      ge = tok_ok ? grad_entropy[tok] : 0.f;
+      He = tok_ok ? entropy[tok] : 0.f;
+    }
+    if (SCALED) {  // the 1/tau of the chain rule, folded into the per-token factors
+      g = g / temperature;
+      ge = ge / temperature;
+    }
 #pragma unroll
     for (int m = 0; m < MSUB; ++m) {
       bf16x4 pk;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int v = vs0 + wv + m * MFMA_MN + acc_row(i, lane);
-        const float p = __builtin_amdgcn_exp2f((acc[m][n][i] - L) * LOG2E);
+        const float z = SCALED ? acc[m][n][i] / temperature : acc[m][n][i];
+        const float lp = z - L;
+        const float p = __builtin_amdgcn_exp2f(lp * LOG2E);
         const float oh = v == y ? 1.f : 0.f;
-        const float d = v < V ? g * (oh - p) : 0.f;
-        pk[i] = (__bf16)d;
+        float d = g * (oh - p);
+        if (EGRAD) d = d - ge * (p * (lp + He));
+        pk[i] = (__bf16)(v < V ? d : 0.f);
       }
       *reinterpret_cast<bf16x4*>(wl + (n * MFMA_MN + j) * DZ_PITCH + (m * MFMA_MN + 4 * g4) * 2) = pk;
     }
@@ -239,6 +257,7 @@ __device__ __forceinline__ void gemm_acc_store(const GemmProblem& p, int m0, int
 template <class Cfg>
 __global__ __launch_bounds__(Cfg::NTHREADS) void gemm_tn_f32_persistent_kernel(GemmProblem p0, GemmProblem p1,
                                                                                int* __restrict__ sched) {
+  loop_placement_pad<8>();
   __shared__ __attribute__((aligned(1024))) char lds[PingPong<Cfg>::LDS_BYTES];
   // tile numbers pass from thread 0 to the workgroup through the first word of B slot 1 (see the
   // forward's persistent kernel)
@@ -372,8 +391,12 @@ void launch_bwd(const BwdArgs& a, hipStream_t stream) {
     {
       const int n_mt = (Vc + CfgDz::TM - 1) / CfgDz::TM;
       const int n_nt = (L.T + CfgDz::TN - 1) / CfgDz::TN;
-      hipLaunchKernelGGL(bwd_dz_kernel<CfgDz>, dim3(n_mt * n_nt), dim3(CfgDz::NTHREADS), 0, stream, a.hidden,
-                         a.weight, a.labels, a.grad, a.lse, L.T, L.H, L.V, vs0, Vc, L.Vs, n_mt, n_nt, dz);
+      const bool scaled = a.temperature != 1.0f, egrad = a.grad_entropy != nullptr;
+      auto kern = scaled ? (egrad ? bwd_dz_kernel<CfgDz, true, true> : bwd_dz_kernel<CfgDz, true, false>)
+                         : (egrad ? bwd_dz_kernel<CfgDz, false, true> : bwd_dz_kernel<CfgDz, false, false>);
+      hipLaunchKernelGGL(kern, dim3(n_mt * n_nt), dim3(CfgDz::NTHREADS), 0, stream, a.hidden, a.weight, a.labels,
+                         a.grad, a.lse, a.grad_entropy, a.entropy, a.temperature, L.T, L.H, L.V, vs0, Vc, L.Vs, n_mt,
+                         n_nt, dz);
     }
     const int Vc8 = (Vc + 7) / 8 * 8;  // dz columns past Vc inside the written tiles are zeros
     GemmProblem pw{}, ph{};

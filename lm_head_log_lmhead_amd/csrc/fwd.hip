@@ -5,16 +5,19 @@
 //    reduction is mostly in-lane).  Its epilogue reduces every (token, 128-entry vocabulary
 //    chunk) to one record {m, n, b, u}:
 //        m = max z,  n = #{z == m},  b = sum_{z < m} exp(z - m),  u = sum exp(z - m) (z - m)
-//    and stores the label's logit when the label falls in the chunk.  Logits never leave the
-//    registers.  (SkyRL PR #1765 "[megatron] Triton backend for fused LM-head log-prob": the
-//    vocab-tiled online softmax that never materializes per-chunk logits, and the -inf masking of
-//    out-of-bounds vocabulary columns in the tail tile.)
+//    (and, when asked, q = sum exp(2 (z - m))) and stores the label's logit when the label falls
+//    in the chunk.  Logits never leave the registers.  (SkyRL PR #1765 "[megatron] Triton backend
+//    for fused LM-head log-prob": the vocab-tiled online softmax that never materializes per-chunk
+//    logits, and the -inf masking of out-of-bounds vocabulary columns in the tail tile.)
+//    With a temperature, every logit is first divided by it in fp32 (verl PR #8026
+//    "batch-invariant actor forward and sampler log-prob formula", review on the temperature
+//    order: fp32 logits divided by the fp32 temperature inside the chunk).
 // K2 fwd_finalize: folds each row's records in a fixed order (64 fixed segments of consecutive
 //    chunks, each folded in ascending order, then the segments in ascending order — a function
 //    of V only) and writes logprob = (z_y - M) - log S, entropy = log S - U/S, lse = M + log S,
-//    with log S = log N + log1p(B/N).  (verl PR #8026, first review: fp32 log_softmax over the
-//    full vocabulary then gather; SkyRL PR #1765, precision-policy commit: logprob 0 for an
-//    out-of-vocabulary label.)
+//    with log S = log N + log1p(B/N), and sum_p2 = Q / S^2.  (verl PR #8026, first review: fp32
+//    log_softmax over the full vocabulary then gather, with entropy and sum_pi_squared of the same
+//    softmax; SkyRL PR #1765, precision-policy commit: logprob 0 for an out-of-vocabulary label.)
 #include "kernels.hpp"
 
 // Build-time tuning knobs (all choices give the same bits: the per-wavefront vocabulary extent
@@ -48,16 +51,31 @@ namespace lmh {
 // it adds exactly zero to every sum (0 * d is -0 for finite d).
 constexpr float MASKED_LOGIT = -1.0e30f;
 
+// Options of the record epilogue, fixed per kernel instantiation.
+template <bool SCALED_, bool P2_>
+struct RecOpt {
+  static constexpr bool SCALED = SCALED_;  // divide every logit by the temperature
+  static constexpr bool P2 = P2_;          // also record q = sum exp(2 (z - m))
+};
+
 // Lane l holds, for each of its NSUB tokens (column l % 16 of an MFMA block), the 32 entries at
 // wavefront rows 16 m + 4 (l / 16) + i; lanes l, l^16, l^32, l^48 together hold the token's 128.
 // lw[n] is the label's offset from wave_v0 for token n * 16 + l % 16 (any value outside [0, 128)
 // when the label is not in this chunk, out of vocabulary, or the token is past T).
-template <int NSUB, bool TAIL>
-__device__ __forceinline__ void fwd_records(f32x4 (&acc)[MSUB][NSUB], int lane, int wave_v0, int tok0, int T,
-                                            int V, const int (&lw)[NSUB], f32x4* __restrict__ rec,
-                                            float* __restrict__ zy, int chunk) {
+template <int NSUB, bool TAIL, class Opt>
+__device__ __forceinline__ void fwd_records(f32x4 (&acc)[MSUB][NSUB], int lane, int wave_v0, int tok0, int V,
+                                            const int (&lw)[NSUB], const FwdArgs& a, int chunk) {
   const int j = acc_col(lane);
   const int g = lane >> 4;
+  if (Opt::SCALED) {
+    const float tau = a.temperature;
+#pragma unroll
+    for (int m = 0; m < MSUB; ++m)
+#pragma unroll
+      for (int n = 0; n < NSUB; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[m][n][i] = acc[m][n][i] / tau;
+  }
   if (TAIL) {
 #pragma unroll
     for (int m = 0; m < MSUB; ++m)
@@ -70,7 +88,7 @@ __device__ __forceinline__ void fwd_records(f32x4 (&acc)[MSUB][NSUB], int lane, 
 #pragma unroll
   for (int n = 0; n < NSUB; ++n) {
     const int tok = tok0 + n * MFMA_MN + j;
-    const bool tok_ok = tok < T;
+    const bool tok_ok = tok < a.T;
 
     // pass 1: chunk max over this lane's 32 entries, then across the four lanes of the token
     float mx = acc[0][n][0];
@@ -83,7 +101,7 @@ __device__ __forceinline__ void fwd_records(f32x4 (&acc)[MSUB][NSUB], int lane, 
 
     // pass 2: count at the max, sum of exp below it, sum of exp * shift (fixed order: m, then i)
     int cnt = 0;
-    float b = 0.f, u = 0.f;
+    float b = 0.f, u = 0.f, q = 0.f;
 #pragma unroll
     for (int m = 0; m < MSUB; ++m)
 #pragma unroll
@@ -94,6 +112,7 @@ __device__ __forceinline__ void fwd_records(f32x4 (&acc)[MSUB][NSUB], int lane, 
         cnt += at_max;
         b += at_max ? 0.f : e;
         u = __builtin_fmaf(e, d, u);
+        if (Opt::P2) q = __builtin_fmaf(e, e, q);
       }
     // the four lanes' partial sums as (s0 + s1) + (s2 + s3): by commutativity of each addition,
     // every lane of the token ends with the same bits
@@ -103,6 +122,10 @@ __device__ __forceinline__ void fwd_records(f32x4 (&acc)[MSUB][NSUB], int lane, 
     cnt += __shfl_xor(cnt, 32);
     b += __shfl_xor(b, 32);
     u += __shfl_xor(u, 32);
+    if (Opt::P2) {
+      q += __shfl_xor(q, 16);
+      q += __shfl_xor(q, 32);
+    }
 
     // label logit: local index w sits in block w / 16, lane group (w % 16) / 4, register w % 4.
     // Few chunks hold a label, so the select runs behind a wavefront-uniform branch.
@@ -115,7 +138,7 @@ __device__ __forceinline__ void fwd_records(f32x4 (&acc)[MSUB][NSUB], int lane, 
       for (int m = 0; m < MSUB; ++m)
 #pragma unroll
         for (int i = 0; i < 4; ++i) val = (idx == m * 4 + i) ? acc[m][n][i] : val;
-      if (mine) zy[tok] = val;
+      if (mine) a.zy[tok] = val;
     }
     if (g == 0 && tok_ok) {
       f32x4 v;
@@ -123,16 +146,23 @@ __device__ __forceinline__ void fwd_records(f32x4 (&acc)[MSUB][NSUB], int lane, 
       v[1] = (float)cnt;
       v[2] = b;
       v[3] = u;
-      rec[(size_t)chunk * (size_t)T + tok] = v;
+      const size_t at = (size_t)chunk * (size_t)a.T + tok;
+      a.rec[at] = v;
+      if (Opt::P2) a.rec2[at] = q;
     }
   }
 }
 
-// The wavefront's labels as offsets from its first vocabulary row (see fwd_records).
+// The wavefront's labels as offsets from its first vocabulary row (see fwd_records); a label
+// outside this call's rows [vocab_start, vocab_start + V) is not in any of its chunks.
 template <int NSUB>
-__device__ __forceinline__ void label_offsets(const int (&y)[NSUB], int wave_v0, int V, int (&lw)[NSUB]) {
+__device__ __forceinline__ void label_offsets(const int (&y)[NSUB], int wave_v0, const FwdArgs& a, int (&lw)[NSUB]) {
 #pragma unroll
-  for (int n = 0; n < NSUB; ++n) lw[n] = (y[n] >= 0 && y[n] < V) ? y[n] - wave_v0 : -1;
+  for (int n = 0; n < NSUB; ++n) {
+    // vocab_start + V <= vocab_total < 2^31, so neither difference overflows
+    const bool in_rows = y[n] >= a.vocab_start && y[n] - a.vocab_start < a.V;
+    lw[n] = in_rows ? y[n] - a.vocab_start - wave_v0 : -1;
+  }
 }
 
 template <int NSUB>
@@ -144,28 +174,26 @@ __device__ __forceinline__ void load_labels(const int* __restrict__ labels, int 
   }
 }
 
-// Records of the wavefront's chunk of the tile at (v0, t0); lw from label_offsets.
-template <class Cfg>
-__device__ __forceinline__ void tile_records(f32x4 (&acc)[MSUB][Cfg::NSUB], int v0, int t0, int T, int V,
-                                             const int (&lw)[Cfg::NSUB], f32x4* __restrict__ rec,
-                                             float* __restrict__ zy) {
+// Records of the wavefront's chunk of the tile at (v0, t0) (local weight rows); lw from
+// label_offsets.
+template <class Cfg, class Opt>
+__device__ __forceinline__ void tile_records(f32x4 (&acc)[MSUB][Cfg::NSUB], int v0, int t0, const int (&lw)[Cfg::NSUB],
+                                             const FwdArgs& a) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave % Cfg::WM, wn = wave / Cfg::WM;
   const int wave_v0 = v0 + wm * WAVE_M;
-  if (wave_v0 >= V) return;  // this wavefront's chunk lies wholly past the vocabulary
+  if (wave_v0 >= a.V) return;  // this wavefront's chunk lies wholly past the weight rows
   const int tok0 = t0 + wn * Cfg::WAVE_N;
-  const int chunk = wave_v0 / WAVE_M;
-  if (wave_v0 + WAVE_M <= V)
-    fwd_records<Cfg::NSUB, false>(acc, lane, wave_v0, tok0, T, V, lw, rec, zy, chunk);
+  const int chunk = (a.vocab_start + wave_v0) / WAVE_M;
+  if (wave_v0 + WAVE_M <= a.V)
+    fwd_records<Cfg::NSUB, false, Opt>(acc, lane, wave_v0, tok0, a.V, lw, a, chunk);
   else
-    fwd_records<Cfg::NSUB, true>(acc, lane, wave_v0, tok0, T, V, lw, rec, zy, chunk);
+    fwd_records<Cfg::NSUB, true, Opt>(acc, lane, wave_v0, tok0, a.V, lw, a, chunk);
 }
 
-template <class Cfg>
-__global__ __launch_bounds__(Cfg::NTHREADS) void fwd_partials_kernel(
-    const __bf16* __restrict__ hidden, const __bf16* __restrict__ weight, const int* __restrict__ labels,
-    int T, int H, int V, int n_mt, int n_nt, f32x4* __restrict__ rec, float* __restrict__ zy) {
+template <class Cfg, class Opt>
+__global__ __launch_bounds__(Cfg::NTHREADS) void fwd_partials_kernel(FwdArgs a, int n_mt, int n_nt) {
   __shared__ __attribute__((aligned(1024))) char lds[Cfg::LDS_BYTES];
   int mt, nt;
   tile_coords<LMH_GROUP_M>(blockIdx.x, gridDim.x, n_mt, n_nt, mt, nt);
@@ -176,16 +204,16 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void fwd_partials_kernel(
   for (int m = 0; m < MSUB; ++m)
 #pragma unroll
     for (int n = 0; n < Cfg::NSUB; ++n) acc[m][n] = (f32x4)(0.0f);
-  const __bf16* A = weight + (int64_t)v0 * H;
-  const __bf16* B = hidden + (int64_t)t0 * H;
-  const int rowsA = min(Cfg::TM, V - v0), rowsB = min(Cfg::TN, T - t0);
+  const __bf16* A = a.weight + (int64_t)v0 * a.H;
+  const __bf16* B = a.hidden + (int64_t)t0 * a.H;
+  const int rowsA = min(Cfg::TM, a.V - v0), rowsB = min(Cfg::TN, a.T - t0);
   static_assert(Cfg::LOOP == LOOP_SPREAD, "one-tile-per-workgroup grid: spread main loop");
-  tile_mainloop_spread<Cfg>(A, H, rowsA, B, H, rowsB, H, lds, acc);
+  tile_mainloop_spread<Cfg>(A, a.H, rowsA, B, a.H, rowsB, a.H, lds, acc);
   const int wave = threadIdx.x >> 6;
   int y[Cfg::NSUB], lw[Cfg::NSUB];
-  load_labels(labels, t0 + (wave / Cfg::WM) * Cfg::WAVE_N, threadIdx.x & 63, T, y);
-  label_offsets(y, v0 + (wave % Cfg::WM) * WAVE_M, V, lw);
-  tile_records<Cfg>(acc, v0, t0, T, V, lw, rec, zy);
+  load_labels(a.labels, t0 + (wave / Cfg::WM) * Cfg::WAVE_N, threadIdx.x & 63, a.T, y);
+  label_offsets(y, v0 + (wave % Cfg::WM) * WAVE_M, a, lw);
+  tile_records<Cfg, Opt>(acc, v0, t0, lw, a);
 }
 
 // Persistent form for the ping-pong tile: one workgroup per CU.
@@ -193,9 +221,9 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void fwd_partials_kernel(
 // Tiles are handed out by a TileQueue over per-XCD counters in the workspace.  A workgroup on XCD
 // x takes the next tile of x's contiguous tile range (so the workgroups of an XCD work on
 // neighbouring tiles together, sharing A and B rows in that XCD's L2); once x's range is used up
-// it takes tiles from the other XCDs' ranges.  XCDs do not run at the same speed, and a static split leaves the fastest
-// idle at the end.  The counters decide only which workgroup computes a tile, never what it
-// computes: every tile's records are the same bits whoever computes them.
+// it takes tiles from the other XCDs' ranges.  XCDs do not run at the same speed, and a static
+// split leaves the fastest idle at the end.  The counters decide only which workgroup computes a
+// tile, never what it computes: every tile's records are the same bits whoever computes them.
 //
 // The claim of the tile after next is issued during the current tile's epilogue and read after
 // the next tile's K loop, so its latency hides behind that loop.  The next tile's first loads are
@@ -206,20 +234,19 @@ __global__ void fwd_sched_reset_kernel(int* __restrict__ sched) {
   if (threadIdx.x < SCHED_WORDS) sched[threadIdx.x] = 0;
 }
 
-template <class Cfg>
-__global__ __launch_bounds__(Cfg::NTHREADS) void fwd_partials_persistent_kernel(
-    const __bf16* __restrict__ hidden, const __bf16* __restrict__ weight, const int* __restrict__ labels,
-    int T, int H, int V, int n_mt, int n_nt, f32x4* __restrict__ rec, float* __restrict__ zy,
-    int* __restrict__ sched) {
+template <class Cfg, class Opt>
+__global__ __launch_bounds__(Cfg::NTHREADS) void fwd_partials_persistent_kernel(FwdArgs a, int n_mt, int n_nt) {
+  loop_placement_pad<2 * Opt::SCALED + Opt::P2>();
   __shared__ __attribute__((aligned(1024))) char lds[Cfg::LDS_BYTES];
   // Tile numbers are passed from thread 0 to the workgroup through the first word of B slot 1,
   // which no load writes between the end of one K loop and the first barrier of the next.
   int* const bc = reinterpret_cast<int*>(lds + PingPong<Cfg>::B_BASE + PingPong<Cfg>::SLOT);
-  const TileQueue q{sched, n_mt * n_nt, 0};
+  const TileQueue q{a.sched, n_mt * n_nt, 0};
   const int xcd = blockIdx.x & 7;
   const int wm = (threadIdx.x >> 6) % Cfg::WM;
   const int wn = (threadIdx.x >> 6) / Cfg::WM;
   const int lane = threadIdx.x & 63;
+  const int H = a.H;
 
   if (threadIdx.x == 0) bc[0] = q.resolve(xcd, q.claim(xcd));
   __syncthreads();
@@ -230,12 +257,13 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void fwd_partials_persistent_kernel(
   int mt, nt;
   group_coords<LMH_GROUP_M>(L, n_mt, n_nt, mt, nt);
   int v0 = mt * Cfg::TM, t0 = nt * Cfg::TN;
-  pp.start(weight + (int64_t)v0 * H, H, min(Cfg::TM, V - v0), hidden + (int64_t)t0 * H, H, min(Cfg::TN, T - t0), H);
+  pp.start(a.weight + (int64_t)v0 * H, H, min(Cfg::TM, a.V - v0), a.hidden + (int64_t)t0 * H, H,
+           min(Cfg::TN, a.T - t0), H);
   int claim = 0;  // thread 0: raw counter value of the next claim on this XCD's range
   if (threadIdx.x == 0) claim = q.claim(xcd);
   for (;;) {
     int y[Cfg::NSUB];
-    load_labels(labels, t0 + wn * Cfg::WAVE_N, lane, T, y);
+    load_labels(a.labels, t0 + wn * Cfg::WAVE_N, lane, a.T, y);
     f32x4 acc[MSUB][Cfg::NSUB];
 #pragma unroll
     for (int m = 0; m < MSUB; ++m)
@@ -245,7 +273,7 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void fwd_partials_persistent_kernel(
     // The labels are consumed here, before the next tile's loads go out: the compiler's wait for
     // them then covers nothing else.
     int lw[Cfg::NSUB];
-    label_offsets(y, v0 + wm * WAVE_M, V, lw);
+    label_offsets(y, v0 + wm * WAVE_M, a, lw);
     if (threadIdx.x == 0) bc[0] = q.resolve(xcd, claim);
     __syncthreads();
     const int Ln = bc[0];
@@ -255,11 +283,11 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void fwd_partials_persistent_kernel(
       group_coords<LMH_GROUP_M>(Ln, n_mt, n_nt, mt, nt);
       v0n = mt * Cfg::TM;
       t0n = nt * Cfg::TN;
-      pp.start(weight + (int64_t)v0n * H, H, min(Cfg::TM, V - v0n), hidden + (int64_t)t0n * H, H,
-               min(Cfg::TN, T - t0n), H);
+      pp.start(a.weight + (int64_t)v0n * H, H, min(Cfg::TM, a.V - v0n), a.hidden + (int64_t)t0n * H, H,
+               min(Cfg::TN, a.T - t0n), H);
       if (threadIdx.x == 0) claim = q.claim(xcd);
     }
-    tile_records<Cfg>(acc, v0, t0, T, V, lw, rec, zy);
+    tile_records<Cfg, Opt>(acc, v0, t0, lw, a);
     if (Ln < 0) break;
     L = Ln;
     v0 = v0n;
@@ -272,12 +300,13 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void fwd_partials_persistent_kernel(
 // ---------------------------------------------------------------------------------------------
 
 struct Rec {
-  float m, n, b, u;
+  float m, n, b, u, q;
 };
 
 // Merge record r into state s (both relative to their own max).  Empty records (n == 0) are the
-// identity.  The three cases keep b and u relative to the larger max, so nothing below the max
-// is ever added to the count n.
+// identity.  The three cases keep b, u and q relative to the larger max, so nothing below the
+// max is ever added to the count n.  With P2 false, q is carried as 0 and not computed.
+template <bool P2>
 __device__ __forceinline__ Rec fold(Rec s, Rec r) {
   if (r.n == 0.f) return s;
   if (s.n == 0.f) return r;
@@ -290,12 +319,14 @@ __device__ __forceinline__ Rec fold(Rec s, Rec r) {
     o.n = r.n;
     o.b = __builtin_fmaf(sn, a, r.b);
     o.u = __builtin_fmaf(__builtin_fmaf(dm, sn, s.u), a, r.u);
+    o.q = P2 ? __builtin_fmaf(s.q, a * a, r.q) : 0.f;
     return o;
   }
   if (r.m == s.m) {
     s.n += r.n;
     s.b += r.b;
     s.u += r.u;
+    if (P2) s.q += r.q;
     return s;
   }
   const float dm = r.m - s.m;
@@ -303,6 +334,7 @@ __device__ __forceinline__ Rec fold(Rec s, Rec r) {
   const float rn = r.b + r.n;
   s.b = __builtin_fmaf(rn, a, s.b);
   s.u = __builtin_fmaf(__builtin_fmaf(dm, rn, r.u), a, s.u);
+  if (P2) s.q = __builtin_fmaf(r.q, a * a, s.q);
   return s;
 }
 
@@ -310,12 +342,12 @@ constexpr int FIN_TOK = 64;   // tokens per workgroup (one per lane)
 constexpr int FIN_WAVES = 16; // wavefronts per workgroup
 constexpr int FIN_NSEG = 64;  // fixed number of fold segments per row
 
-__global__ __launch_bounds__(FIN_TOK * FIN_WAVES) void fwd_finalize_kernel(
-    const f32x4* __restrict__ rec, const float* __restrict__ zy, const int* __restrict__ labels, int T,
-    int V, int n_c, float* __restrict__ logprob, float* __restrict__ entropy, float* __restrict__ lse) {
+template <bool P2>
+__global__ __launch_bounds__(FIN_TOK * FIN_WAVES) void fwd_finalize_kernel(FwdArgs a, int n_c) {
   __shared__ Rec part[FIN_NSEG][FIN_TOK];
   constexpr int SEG_PER_WAVE = FIN_NSEG / FIN_WAVES;
   constexpr int BATCH = 4;  // records per segment loaded before folding: 16 loads in flight
+  const int T = a.T;
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int t = blockIdx.x * FIN_TOK + lane;
@@ -329,57 +361,79 @@ __global__ __launch_bounds__(FIN_TOK * FIN_WAVES) void fwd_finalize_kernel(
     lo[j] = (int)((int64_t)s * n_c / FIN_NSEG);
     len[j] = (int)((int64_t)(s + 1) * n_c / FIN_NSEG) - lo[j];
     maxlen = max(maxlen, len[j]);
-    seg[j] = Rec{-__builtin_inff(), 0.f, 0.f, 0.f};
+    seg[j] = Rec{-__builtin_inff(), 0.f, 0.f, 0.f, 0.f};
   }
   // Each segment is folded in ascending chunk order; the loads of a batch are all issued first.
   for (int b = 0; b < maxlen; b += BATCH) {
     f32x4 r[SEG_PER_WAVE][BATCH];
+    float r2[SEG_PER_WAVE][BATCH];
 #pragma unroll
     for (int j = 0; j < SEG_PER_WAVE; ++j)
 #pragma unroll
       for (int i = 0; i < BATCH; ++i) {
         const int c = b + i;
-        r[j][i] = (t_ok && c < len[j]) ? rec[(size_t)(lo[j] + c) * (size_t)T + t] : (f32x4)(0.f);
+        const bool ok = t_ok && c < len[j];
+        const size_t at = (size_t)(lo[j] + c) * (size_t)T + t;
+        r[j][i] = ok ? a.rec[at] : (f32x4)(0.f);
+        r2[j][i] = (P2 && ok) ? a.rec2[at] : 0.f;
       }
 #pragma unroll
     for (int j = 0; j < SEG_PER_WAVE; ++j)
 #pragma unroll
-      for (int i = 0; i < BATCH; ++i) seg[j] = fold(seg[j], Rec{r[j][i][0], r[j][i][1], r[j][i][2], r[j][i][3]});
+      for (int i = 0; i < BATCH; ++i)
+        seg[j] = fold<P2>(seg[j], Rec{r[j][i][0], r[j][i][1], r[j][i][2], r[j][i][3], r2[j][i]});
   }
 #pragma unroll
   for (int j = 0; j < SEG_PER_WAVE; ++j) part[w + FIN_WAVES * j][lane] = seg[j];
   __syncthreads();
   if (w != 0 || t >= T) return;
-  Rec st = {-__builtin_inff(), 0.f, 0.f, 0.f};
+  Rec st = {-__builtin_inff(), 0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
-  for (int s = 0; s < FIN_NSEG; ++s) st = fold(st, part[s][lane]);
+  for (int s = 0; s < FIN_NSEG; ++s) st = fold<P2>(st, part[s][lane]);
 
   const float logS = logf(st.n) + log1pf(st.b / st.n);
-  const int y = labels[t];
-  const bool in_vocab = y >= 0 && y < V;
-  logprob[t] = in_vocab ? (zy[t] - st.m) - logS : 0.f;
-  if (entropy) entropy[t] = logS - st.u / (st.n + st.b);
-  if (lse) lse[t] = st.m + logS;
+  const int y = a.labels[t];
+  const bool in_vocab = y >= 0 && y < a.vocab_total;
+  a.logprob[t] = in_vocab ? (a.zy[t] - st.m) - logS : 0.f;
+  if (a.entropy) a.entropy[t] = logS - st.u / (st.n + st.b);
+  if (a.lse) a.lse[t] = st.m + logS;
+  if (P2) {
+    const float S = st.n + st.b;
+    a.sum_p2[t] = st.q / (S * S);
+  }
 }
 
 // ---------------------------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------------------------
 
-template <class Cfg>
-static void launch_partials_cfg(const FwdArgs& a, hipStream_t stream) {
+template <class Cfg, class Opt>
+static void launch_partials_opt(const FwdArgs& a, hipStream_t stream) {
   const int n_mt = (a.V + Cfg::TM - 1) / Cfg::TM;
   const int n_nt = (a.T + Cfg::TN - 1) / Cfg::TN;
   if constexpr (Cfg::LOOP == LOOP_PINGPONG) {
     // one workgroup per CU (the tile takes all of a CU's LDS)
     const int ntiles = n_mt * n_nt;
     hipLaunchKernelGGL(fwd_sched_reset_kernel, dim3(1), dim3(64), 0, stream, a.sched);
-    hipLaunchKernelGGL(fwd_partials_persistent_kernel<Cfg>, dim3(min(ntiles, a.cus)), dim3(Cfg::NTHREADS), 0,
-                       stream, a.hidden, a.weight, a.labels, a.T, a.H, a.V, n_mt, n_nt, a.rec, a.zy, a.sched);
+    hipLaunchKernelGGL((fwd_partials_persistent_kernel<Cfg, Opt>), dim3(min(ntiles, a.cus)), dim3(Cfg::NTHREADS), 0,
+                       stream, a, n_mt, n_nt);
   } else {
-    hipLaunchKernelGGL(fwd_partials_kernel<Cfg>, dim3(n_mt * n_nt), dim3(Cfg::NTHREADS), 0, stream, a.hidden,
-                       a.weight, a.labels, a.T, a.H, a.V, n_mt, n_nt, a.rec, a.zy);
+    hipLaunchKernelGGL((fwd_partials_kernel<Cfg, Opt>), dim3(n_mt * n_nt), dim3(Cfg::NTHREADS), 0, stream, a, n_mt,
+                       n_nt);
   }
+}
+
+template <class Cfg>
+static void launch_partials_cfg(const FwdArgs& a, hipStream_t stream) {
+  const bool scaled = a.temperature != 1.0f;
+  if (scaled && a.want_p2)
+    launch_partials_opt<Cfg, RecOpt<true, true>>(a, stream);
+  else if (scaled)
+    launch_partials_opt<Cfg, RecOpt<true, false>>(a, stream);
+  else if (a.want_p2)
+    launch_partials_opt<Cfg, RecOpt<false, true>>(a, stream);
+  else
+    launch_partials_opt<Cfg, RecOpt<false, false>>(a, stream);
 }
 
 // Tile configurations, chosen by T.  Each has a 128-entry vocabulary extent per wavefront and the
@@ -412,10 +466,12 @@ void launch_fwd_partials(const FwdArgs& a, hipStream_t stream) {
 }
 
 void launch_fwd_finalize(const FwdArgs& a, hipStream_t stream) {
-  const int n_c = (a.V + WAVE_M - 1) / WAVE_M;
+  const int n_c = (a.vocab_total + WAVE_M - 1) / WAVE_M;
   const int nblk = (a.T + FIN_TOK - 1) / FIN_TOK;
-  hipLaunchKernelGGL(fwd_finalize_kernel, dim3(nblk), dim3(FIN_TOK * FIN_WAVES), 0, stream, a.rec, a.zy, a.labels,
-                     a.T, a.V, n_c, a.logprob, a.entropy, a.lse);
+  if (a.sum_p2)
+    hipLaunchKernelGGL(fwd_finalize_kernel<true>, dim3(nblk), dim3(FIN_TOK * FIN_WAVES), 0, stream, a, n_c);
+  else
+    hipLaunchKernelGGL(fwd_finalize_kernel<false>, dim3(nblk), dim3(FIN_TOK * FIN_WAVES), 0, stream, a, n_c);
 }
 
 }  // namespace lmh

@@ -23,14 +23,20 @@ struct FwdArgs {
   const __bf16* hidden;
   const __bf16* weight;
   const int* labels;
-  int T, H, V;
-  f32x4* rec;   // [n_c][T] records
-  float* zy;    // [T] label logits
-  int* sched;   // [SCHED_WORDS] tile counters, reset by the partials launch
+  int T, H, V;        // V: weight rows of this call
+  int vocab_start;    // vocabulary id of weight row 0 (a multiple of VOCAB_CHUNK)
+  int vocab_total;    // vocabulary the records and the fold cover (vocab_start + V <= vocab_total)
+  float temperature;  // the logits are divided by it before the softmax (1: no division)
+  int want_p2;        // also record sum exp(2 (z - max)) per chunk
+  f32x4* rec;         // [n_c][T] records, n_c = ceil(vocab_total / VOCAB_CHUNK)
+  float* rec2;        // [n_c][T] sum of exp(2 (z - max)) per chunk
+  float* zy;          // [T] label logits (divided by the temperature)
+  int* sched;         // [SCHED_WORDS] tile counters, reset by the partials launch
   float* logprob;
   float* entropy;
   float* lse;
-  int cus;      // compute units of the device (persistent grids)
+  float* sum_p2;
+  int cus;            // compute units of the device (persistent grids)
 };
 
 void launch_fwd_partials(const FwdArgs& a, hipStream_t stream);
@@ -50,8 +56,11 @@ struct BwdArgs {
   const __bf16* hidden;
   const __bf16* weight;
   const int* labels;
-  const float* grad;
-  const float* lse;
+  const float* grad;          // [T] upstream gradient of the log-probs
+  const float* lse;           // [T] of the logits divided by the temperature
+  const float* grad_entropy;  // [T] upstream gradient of the entropies, or null
+  const float* entropy;       // [T] forward entropies (needed with grad_entropy)
+  float temperature;
   float* grad_hidden;
   float* grad_weight;
   int accumulate_gw;

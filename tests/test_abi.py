@@ -53,8 +53,8 @@ def test_workspace_sizes(lib):
     T, H, V = 8192, 4096, 152064
     n_c = (V + 127) // 128
     fwd = lmh.lmhead_logprob_fwd_workspace_size(T, H, V)
-    assert fwd >= n_c * T * 16 + T * 4 and fwd % 256 == 0
-    assert lmh.lmhead_logprob_fwd_workspace_size(0, H, V) > 0 or True
+    assert fwd >= n_c * T * 20 + T * 4 and fwd % 256 == 0
+    assert lmh.lmhead_logprob_fwd_workspace_size(0, H, V) > 0       # the scheduler counters
     assert lmh.lmhead_logprob_fwd_workspace_size(4, 12, 10) == 0     # H % 8 != 0
     assert lmh.lmhead_logprob_fwd_workspace_size(-1, 8, 10) == 0
     assert lmh.lmhead_logprob_fwd_workspace_size(4, 8, 0) == 0
@@ -115,3 +115,46 @@ def test_bwd_validation_codes(lib):
     assert call(T=0, h=None, w=None, y=None, g=None, lse=None) == lmh.LMH_OK
     # no gradient requested: validated, nothing to do
     assert call(gh=None, gw=None) == lmh.LMH_OK
+
+
+def test_extended_entry_validation_codes(lib):
+    nan = float("nan")
+
+    def fwd_ex(temp=1.0, **kw):
+        a = dict(h=16, w=16, y=16, T=4, H=8, V=10, lp=16, ent=None, lse=None, p2=None, ws=256, wsb=1 << 20)
+        a.update(kw)
+        return lib.lmhead_logprob_fwd_ex(a["h"], a["w"], a["y"], a["T"], a["H"], a["V"], temp, a["lp"], a["ent"],
+                                         a["lse"], a["p2"], a["ws"], a["wsb"], None)
+
+    for bad in (0.0, -0.7, nan, float("inf")):
+        assert fwd_ex(bad) == lmh.LMH_ERR_INVALID_ARG
+    assert fwd_ex(0.7, p2=6) == lmh.LMH_ERR_UNSUPPORTED
+    assert fwd_ex(0.7, wsb=64) == lmh.LMH_ERR_WORKSPACE_TOO_SMALL
+    # the forward workspace also holds the squared-sum records: strictly larger than the records
+    assert lmh.lmhead_logprob_fwd_workspace_size(64, 8, 1000) >= 64 * 8 * 20
+
+    def part(vs, vt, V=256, temp=1.0, p2=0, wsb=1 << 22):
+        return lib.lmhead_logprob_fwd_partials_ex(16, 16, 16, 4, 8, V, temp, vs, vt, p2, 256, wsb, None)
+
+    assert part(0, 128, V=256) == lmh.LMH_ERR_INVALID_ARG          # shard past the vocabulary
+    assert part(-128, 1024) == lmh.LMH_ERR_INVALID_ARG
+    assert part(64, 1024) == lmh.LMH_ERR_UNSUPPORTED               # not on a 128-row chunk
+    assert part(0, 1024, V=200) == lmh.LMH_ERR_UNSUPPORTED         # partial chunk in a middle shard
+    assert part(0, 1024, p2=2) == lmh.LMH_ERR_INVALID_ARG
+    assert part(0, 1024, temp=nan) == lmh.LMH_ERR_INVALID_ARG
+    assert part(0, 1024, wsb=64) == lmh.LMH_ERR_WORKSPACE_TOO_SMALL
+    assert lib.lmhead_logprob_fwd_finalize_ex(16, 4, 8, 10, 16, None, None, 6, 256, 1 << 20, None) == \
+        lmh.LMH_ERR_UNSUPPORTED
+
+    def bwd_ex(temp=1.0, **kw):
+        a = dict(h=16, w=16, y=16, T=4, H=8, V=10, g=16, lse=16, ge=None, ent=None, gh=16, gw=16, acc=0, ws=256,
+                 wsb=1 << 30)
+        a.update(kw)
+        return lib.lmhead_logprob_bwd_ex(a["h"], a["w"], a["y"], a["T"], a["H"], a["V"], temp, a["g"], a["lse"],
+                                         a["ge"], a["ent"], a["gh"], a["gw"], a["acc"], a["ws"], a["wsb"], None)
+
+    assert bwd_ex(0.0) == lmh.LMH_ERR_INVALID_ARG
+    assert bwd_ex(1.0, ge=16) == lmh.LMH_ERR_INVALID_ARG            # entropy gradient without the entropy
+    assert bwd_ex(1.0, ge=16, ent=6) == lmh.LMH_ERR_UNSUPPORTED
+    assert bwd_ex(1.3, wsb=64) == lmh.LMH_ERR_WORKSPACE_TOO_SMALL
+    assert bwd_ex(1.3, gh=None, gw=None, ge=16, ent=16) == lmh.LMH_OK
