@@ -22,6 +22,7 @@ import re
 import sys
 import time
 
+import numpy as np
 import torch
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -72,7 +73,7 @@ def measured_traffic(workload: str):
     return float(t.group(1))
 
 
-def cpu_baseline(x, rows: int, name: str):
+def cpu_baseline(x, rows: int, name: str, temperature: float = 1.0, sum_p2: bool = False):
     """Times the fp64 CPU oracle (as it stands) on the first `rows` rows of the same inputs."""
     from oracle import fp64
     try:
@@ -84,7 +85,7 @@ def cpu_baseline(x, rows: int, name: str):
     y = x.labels[:rows]
     W = fp64.to_f64(x.weight)          # conversion is outside the timed region
     t0 = time.perf_counter()
-    fp64.forward(h, W, y, entropy=True)
+    fp64.forward(h, W, y, entropy=True, temperature=temperature, sum_p2=sum_p2)
     dt = time.perf_counter() - t0
     return {"value": rows / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": f"first {rows} of {x.hidden.shape[0]} rows of {name} (fp64 numpy, logprob+entropy), "
@@ -102,20 +103,31 @@ def main():
         sys.exit(2)
     wl = synth.WORKLOADS[a.workload]
     T, H, V = wl.T, wl.H, wl.V
+    tau = float(np.float32(wl.temperature))
     dev = torch.device("cuda:0")
     print(f"[bench] generating {a.workload}", file=sys.stderr, flush=True)
     x = synth.make_workload(a.workload, seed=0)
     h, w, y = x.hidden.to(dev), x.weight.to(dev), x.labels.to(dev)
     lp = torch.empty(T, dtype=torch.float32, device=dev)
-    ent = torch.empty(T, dtype=torch.float32, device=dev) if wl.entropy else None
+    ent = torch.empty(T, dtype=torch.float32, device=dev) if (wl.entropy or wl.entropy_grad) else None
     lse = torch.empty(T, dtype=torch.float32, device=dev)
+    p2 = torch.empty(T, dtype=torch.float32, device=dev) if wl.sum_p2 else None
     ws = torch.empty(lmh.lmhead_logprob_fwd_workspace_size(T, H, V), dtype=torch.uint8, device=dev)
+    # vocabulary shards: the step runs shard 0's partials, then the fold over every shard's records
+    shards = synth.shard_bounds(V, wl.shards)
+    v0, v1 = shards[0]
+    Vp = v1 - v0                        # weight rows the partials stage computes per step
     if wl.backward:
         g = x.grad.to(dev)
+        ge = x.grad_entropy.to(dev) if x.grad_entropy is not None else None
         gh = torch.empty((T, H), dtype=torch.float32, device=dev)
         gw = torch.empty((V, H), dtype=torch.float32, device=dev)
         wsb = torch.empty(lmh.lmhead_logprob_bwd_workspace_size(T, H, V), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
+    extended = tau != 1.0 or wl.sum_p2 or wl.shards > 1 or wl.entropy_grad
+    if wl.shards > 1:   # every shard's records, once, so the fold reads real data
+        for s0, s1 in shards:
+            lmh.lmhead_logprob_fwd_partials_ex(h, w[s0:s1], y, tau, s0, V, wl.sum_p2, ws, stream)
 
     if a.copy_bytes:
         src = torch.empty(a.copy_bytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
@@ -129,14 +141,24 @@ def main():
     def step(evs=None):
         if evs is not None:
             evs[0].record(stream)
-        lmh.lmhead_logprob_fwd_partials(h, w, y, ws, stream)
+        if extended:
+            lmh.lmhead_logprob_fwd_partials_ex(h, w[v0:v1], y, tau, v0, V, wl.sum_p2, ws, stream)
+        else:
+            lmh.lmhead_logprob_fwd_partials(h, w, y, ws, stream)
         if evs is not None:
             evs[1].record(stream)
-        lmh.lmhead_logprob_fwd_finalize(y, T, H, V, lp, ent, lse, ws, stream)
+        if extended:
+            lmh.lmhead_logprob_fwd_finalize_ex(y, T, H, V, lp, ent, lse, p2, ws, stream)
+        else:
+            lmh.lmhead_logprob_fwd_finalize(y, T, H, V, lp, ent, lse, ws, stream)
         if evs is not None:
             evs[2].record(stream)
         if wl.backward:
-            lmh.lmhead_logprob_bwd(h, w, y, g, lse, gh, gw, False, wsb, stream)
+            if extended:
+                lmh.lmhead_logprob_bwd_ex(h, w, y, tau, g, lse, ge, ent if ge is not None else None, gh, gw, False,
+                                          wsb, stream)
+            else:
+                lmh.lmhead_logprob_bwd(h, w, y, g, lse, gh, gw, False, wsb, stream)
             if evs is not None:
                 evs[3].record(stream)
 
@@ -156,19 +178,20 @@ def main():
     k2 = sum(e[1].elapsed_time(e[2]) for e in evs) / a.steps       # ms, stage 2 (fold)
     kb = sum(e[2].elapsed_time(e[3]) for e in evs) / a.steps if wl.backward else 0.0
     ms = wall * 1e3 / a.steps
-    fwd_flops = 2.0 * T * H * V
-    flops = fwd_flops * (4.0 if wl.backward else 1.0)   # backward: recompute + two gradient GEMMs
-    alg_bytes = 2.0 * V * H + 2.0 * T * H + 12.0 * T     # W once, h once, labels + outputs
+    fwd_flops = 2.0 * T * H * Vp                          # the partials stage's logit tiles
+    flops = 2.0 * T * H * V * (4.0 if wl.backward else 1.0) if wl.shards == 1 else fwd_flops
+    alg_bytes = 2.0 * Vp * H + 2.0 * T * H + 12.0 * T     # W (or its shard) once, h once, labels + outputs
     k1_tflops = fwd_flops / (k1 * 1e-3) / 1e12
     k1_gbs = alg_bytes / (k1 * 1e-3) / 1e9
     # W (2VH bytes) streamed once for 2TVH flops: T flop/B; below the ridge the kernel is HBM-bound
     hbm_bound = T < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
     traffic = measured_traffic(a.workload)
+    kname = "fwd_partials_persistent_kernel" if T > 64 else "fwd_partials_kernel"
     if hbm_bound:
-        roof = {"bound": "hbm", "kernel": "fwd_partials_kernel", "achieved": k1_gbs, "peak": PEAK_HBM_GBS,
+        roof = {"bound": "hbm", "kernel": kname, "achieved": k1_gbs, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": k1_gbs / PEAK_HBM_GBS, "traffic": traffic}
     else:
-        roof = {"bound": "mfma", "kernel": "fwd_partials_kernel", "achieved": k1_tflops, "peak": PEAK_BF16_TFLOPS,
+        roof = {"bound": "mfma", "kernel": kname, "achieved": k1_tflops, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": k1_tflops / PEAK_BF16_TFLOPS, "traffic": traffic}
     out = {
         "metric": METRIC,
@@ -184,7 +207,10 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": a.workload, "T": T, "H": H, "V": V, "entropy": bool(wl.entropy),
-                   "backward": bool(wl.backward)},
+                   "backward": bool(wl.backward),
+                   **({"temperature": tau} if tau != 1.0 else {}), **({"sum_p2": True} if wl.sum_p2 else {}),
+                   **({"entropy_grad": True} if wl.entropy_grad else {}),
+                   **({"vocab_shard": [v0, v1], "shards": wl.shards} if wl.shards > 1 else {})},
         "tflops": flops / (ms * 1e-3) / 1e12,
         "pct_bf16_mfma_peak": 100.0 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "stage_ms": {"fwd_partials": k1, "fwd_finalize": k2, **({"bwd": kb} if wl.backward else {})},
@@ -196,7 +222,7 @@ def main():
         out["bwd_tflops"] = 6.0 * T * H * V / (kb * 1e-3) / 1e12
     if a.cpu_sample_rows > 0:
         print(f"[bench] timing the CPU oracle on {a.cpu_sample_rows} rows", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(x, min(a.cpu_sample_rows, T), a.workload)
+        out["cpu_baseline"] = cpu_baseline(x, min(a.cpu_sample_rows, T), a.workload, tau, wl.sum_p2)
     print(json.dumps(out), flush=True)
 
 

@@ -11,7 +11,7 @@ tensors at the same hidden and vocabulary sizes stand in for them.
 
 Streams: every tensor of a case draws from its own generator, seeded with ``16*seed + stream``:
 hidden = 0, weight = 1, labels = 2, peaked-row permutation = 3, probe placement = 4,
-upstream gradient = 5.
+upstream gradient of the log-probs = 5, upstream gradient of the entropies = 6.
 """
 from __future__ import annotations
 
@@ -26,6 +26,7 @@ STREAM_LABELS = 2
 STREAM_PEAK = 3
 STREAM_PLACE = 4
 STREAM_GRAD = 5
+STREAM_GRAD_ENTROPY = 6
 
 
 def generator(seed: int, stream: int) -> torch.Generator:
@@ -71,6 +72,18 @@ def upstream_grad(T: int, seed: int = 0) -> torch.Tensor:
     return torch.randn((T,), generator=generator(seed, STREAM_GRAD), dtype=torch.float32)
 
 
+def entropy_grad(T: int, seed: int = 0) -> torch.Tensor:
+    """fp32 [T], N(0, 1): the gradient arriving on the entropies."""
+    return torch.randn((T,), generator=generator(seed, STREAM_GRAD_ENTROPY), dtype=torch.float32)
+
+
+def shard_bounds(V: int, shards: int, chunk: int = 128):
+    """[(start, end)] of `shards` vocabulary shards on `chunk`-row boundaries: every shard but the
+    last has ceil(V / shards / chunk) chunks."""
+    size = -(-V // (shards * chunk)) * chunk
+    return [(min(V, k * size), min(V, (k + 1) * size)) for k in range(shards)]
+
+
 def placement(n: int, T: int, seed: int = 0, salt: int = 0) -> torch.Tensor:
     """n distinct row positions in [0, T), seeded (used to embed probe rows in filler batches)."""
     g = generator(seed, STREAM_PLACE)
@@ -90,6 +103,10 @@ class Workload:
     peaked_frac: float = 0.0
     entropy: bool = True
     backward: bool = False
+    temperature: float = 1.0      # logits divided by this fp32 value
+    sum_p2: bool = False          # also sum_j p_j^2
+    entropy_grad: bool = False    # backward also carries an upstream gradient on the entropies
+    shards: int = 1               # > 1: the step is shard 0 of this many vocabulary shards, then the fold
 
 
 # The workloads the measurements are quoted on (names say what they are).
@@ -102,6 +119,13 @@ WORKLOADS = {
     "fwd_T64_H5120_V152064": Workload("fwd_T64_H5120_V152064", 64, 5120, 152064),
     "fwd_T256_H5120_V152064": Workload("fwd_T256_H5120_V152064", 256, 5120, 152064),
     "fwdbwd_T4096_H5120_V152064": Workload("fwdbwd_T4096_H5120_V152064", 4096, 5120, 152064, backward=True),
+    # the extended entry points at the same sizes
+    "fwd_T8192_H4096_V152064_peaked_tau0.7_p2": Workload("fwd_T8192_H4096_V152064_peaked_tau0.7_p2", 8192, 4096,
+                                                         152064, peaked_frac=0.01, temperature=0.7, sum_p2=True),
+    "fwd_T8192_H4096_V152064_peaked_shard0of8": Workload("fwd_T8192_H4096_V152064_peaked_shard0of8", 8192, 4096,
+                                                         152064, peaked_frac=0.01, shards=8),
+    "fwdbwd_T4096_H5120_V152064_tau0.7_egrad": Workload("fwdbwd_T4096_H5120_V152064_tau0.7_egrad", 4096, 5120, 152064,
+                                                        backward=True, temperature=0.7, entropy_grad=True),
 }
 
 
@@ -111,6 +135,7 @@ class Inputs:
     weight: torch.Tensor          # bf16 [V, H]
     labels: torch.Tensor          # int32 [T]
     grad: Optional[torch.Tensor]  # fp32 [T] or None
+    grad_entropy: Optional[torch.Tensor] = None  # fp32 [T] or None
 
 
 def make_inputs(T: int, H: int, V: int, seed: int = 0, hidden_std: float = 1.0,
@@ -125,4 +150,7 @@ def make_inputs(T: int, H: int, V: int, seed: int = 0, hidden_std: float = 1.0,
 
 def make_workload(name: str, seed: int = 0) -> Inputs:
     w = WORKLOADS[name]
-    return make_inputs(w.T, w.H, w.V, seed, w.hidden_std, w.weight_std, w.peaked_frac, with_grad=w.backward)
+    x = make_inputs(w.T, w.H, w.V, seed, w.hidden_std, w.weight_std, w.peaked_frac, with_grad=w.backward)
+    if w.entropy_grad:
+        x.grad_entropy = entropy_grad(w.T, seed)
+    return x
