@@ -9,9 +9,10 @@
 //
 // The vocabulary is walked in fixed steps of Vs rows.  Per step:
 //   K3 bwd_dz     : logit tile recompute (same MFMA main loop and tiles as the forward) and
-//                   dz rounded to bf16, written token-major into a [T x Vs] workspace slab;
-//   transposes    : dz -> dz^T [Vs x Tp] and W_step -> W_step^T [H x Vs] (token- / vocab-
-//                   contiguous copies, so both gradient GEMMs read K-contiguous operands);
+//                   dz rounded to bf16, written both token-major into a [T x Vs] workspace slab
+//                   and vocabulary-major into a [Vs x Tp] slab (dz^T);
+//   transpose     : W_step -> W_step^T [H x Vs] (a vocabulary-contiguous copy, so both gradient
+//                   GEMMs read K-contiguous operands; h^T [H x Tp] is made once per call);
 //   K5 grad_weight: grad_W[step rows] (+)= dz^T . h  (K = tokens, one chain per element, no split)
 //   K4 grad_hidden: grad_h += dz . W_step           (K = vocabulary; the accumulator is loaded
 //                   from grad_h so the chain simply continues across steps)
@@ -36,7 +37,7 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void bwd_dz_kernel(
     const __bf16* __restrict__ hidden, const __bf16* __restrict__ weight, const int* __restrict__ labels,
     const float* __restrict__ grad, const float* __restrict__ lse, const float* __restrict__ grad_entropy,
     const float* __restrict__ entropy, float temperature, int T, int H, int V, int vs0, int Vc, int Vs, int n_mt,
-    int n_nt, __bf16* __restrict__ dz) {
+    int n_nt, __bf16* __restrict__ dz, __bf16* __restrict__ dzt, int ldt) {
   loop_placement_pad<4 + 2 * SCALED + EGRAD>();
   constexpr int STAGE_OUT = Cfg::NWAVES * Cfg::WAVE_N * DZ_PITCH;
   constexpr int LDS = PingPong<Cfg>::LDS_BYTES > STAGE_OUT ? PingPong<Cfg>::LDS_BYTES : STAGE_OUT;
@@ -92,7 +93,7 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void bwd_dz_kernel(
         const float oh = v == y ? 1.f : 0.f;
         float d = g * (oh - p);
         if (EGRAD) d = d - ge * (p * (lp + He));
-        pk[i] = (__bf16)(v < V ? d : 0.f);
+        pk[i] = (__bf16)(v < V && tok_ok ? d : 0.f);
       }
       *reinterpret_cast<bf16x4*>(wl + (n * MFMA_MN + j) * DZ_PITCH + (m * MFMA_MN + 4 * g4) * 2) = pk;
     }
@@ -108,6 +109,27 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void bwd_dz_kernel(
     const int tok = tok0 + row;
     const u32x4 v = *reinterpret_cast<const u32x4*>(wl + row * DZ_PITCH + c * 16);
     if (tok < T) *reinterpret_cast<u32x4*>(dz + (int64_t)tok * Vs + wv + c * 8) = v;
+  }
+  // dz^T: the same staged block read by transposing LDS reads.  A 16-lane group takes a job of
+  // 16 entries x 8 tokens: lane 4 e + q of the group addresses token rows 8 tb + e and 8 tb + 4 + e
+  // at entries 16 vb + 4 q .. + 3, and lane i receives entry 16 vb + i of the 8 tokens, one
+  // 16-byte run of a dz^T row.  Tokens past T within a written run are zeros.
+  {
+    constexpr int TB = Cfg::WAVE_N / 8, JOBS = (WAVE_M / 16) * TB;
+    const int jj = lane & 15;
+    const uint32_t a0 = lds_addr(wl) + (jj >> 2) * DZ_PITCH + (jj & 3) * 8;
+#pragma unroll
+    for (int it = 0; it < JOBS / 4; ++it) {
+      const int job = it * 4 + g4;
+      const int vb = job / TB, tb = job % TB;
+      const uint32_t a = a0 + 8 * tb * DZ_PITCH + 32 * vb;
+      const s16x4 lo = ds_read_tr16(a);
+      const s16x4 hi = ds_read_tr16(a + 4 * DZ_PITCH);
+      const int tok = tok0 + 8 * tb;
+      if (tok < T)
+        *reinterpret_cast<u32x4*>(dzt + (int64_t)(wv + 16 * vb + jj) * ldt + tok) =
+            __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
   }
 }
 
@@ -396,12 +418,12 @@ void launch_bwd(const BwdArgs& a, hipStream_t stream) {
                          : (egrad ? bwd_dz_kernel<CfgDz, false, true> : bwd_dz_kernel<CfgDz, false, false>);
       hipLaunchKernelGGL(kern, dim3(n_mt * n_nt), dim3(CfgDz::NTHREADS), 0, stream, a.hidden, a.weight, a.labels,
                          a.grad, a.lse, a.grad_entropy, a.entropy, a.temperature, L.T, L.H, L.V, vs0, Vc, L.Vs, n_mt,
-                         n_nt, dz);
+                         n_nt, dz, dzt, L.Tp);
     }
-    const int Vc8 = (Vc + 7) / 8 * 8;  // dz columns past Vc inside the written tiles are zeros
+    // dz^T rows hold tokens up to T rounded up to 8 (zeros past T); the gradient GEMM reads no
+    // 16-byte chunk that starts at or past T
     GemmProblem pw{}, ph{};
     if (a.grad_weight) {
-      launch_transpose(dz, L.Vs, L.T, Vc8, dzt, L.Tp, L.Tp, stream);
       pw = make_problem<CfgGrad>(dzt, L.Tp, Vc, ht, L.Tp, L.H, L.T, a.grad_weight + (int64_t)vs0 * L.H, L.H,
                                  a.accumulate_gw);
     }

@@ -26,6 +26,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int MFMA_MN = 16;            // rows and columns of one MFMA output block
 constexpr int MFMA_K = 32;             // k extent of one MFMA
@@ -189,6 +190,14 @@ __device__ __forceinline__ void dma16(u32x4 desc, uint32_t voff, uint32_t lds_ba
       :
       : "v"(voff), "s"(desc), "s"(lds_base)
       : "memory");
+}
+
+// ds_read_b64_tr_b16 at LDS byte address `addr` (8-byte aligned).  In each group of 16 lanes,
+// lane i receives element i % 4 of the 8 bytes addressed by lane 4 e + i / 4 of its group as its
+// element e: if those four lanes address four consecutive 4-element pieces of one row of a 2-byte
+// matrix, and the group's lanes 4 e + q take row e, lane i gets column i of the 4 x 16 block.
+__device__ __forceinline__ s16x4 ds_read_tr16(uint32_t addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(uintptr_t)addr);
 }
 
 template <int N>
