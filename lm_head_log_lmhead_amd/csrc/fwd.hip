@@ -26,9 +26,10 @@
 #ifndef LMH_GROUP_M
 #define LMH_GROUP_M 8
 #endif
-// small-T tiles (T <= 32 and 32 < T <= 64): stages and K step of the spread main loop
+// small-T tiles (T <= 32 and 32 < T <= 64): wavefront grid (WM, WN, NSUB), stages and K step of
+// the spread main loop
 #ifndef LMH_SMALL_NS
-#define LMH_SMALL_NS 4
+#define LMH_SMALL_NS 5
 #endif
 #ifndef LMH_SMALL_BK
 #define LMH_SMALL_BK 64
@@ -38,6 +39,12 @@
 #endif
 #ifndef LMH_S64_BK
 #define LMH_S64_BK 64
+#endif
+#ifndef LMH_SMALL_SHAPE
+#define LMH_SMALL_SHAPE 1, 2, 1
+#endif
+#ifndef LMH_S64_SHAPE
+#define LMH_S64_SHAPE 1, 4, 1
 #endif
 
 namespace lmh {
@@ -450,11 +457,16 @@ struct FwdCfg : P {
 // From T = 96 up it beat a 4-wavefront 256 x 128 tile everywhere measured, even where most of
 // its token columns are empty: the weight stream, not the MFMA work, sets the time there.
 using CfgBig = FwdCfg<PipeCfg<2, 4, 4, 2, 64>, LOOP_PINGPONG>;
-// T <= 32: 256 vocab x 32 tokens, 2 wavefronts, four stages of K = 64 with the loads spread between
-// the MFMAs: the weight stream is HBM-bound here, so deep prefetch matters most
-using CfgSmall = FwdCfg<PipeCfg<2, 1, 2, LMH_SMALL_NS, LMH_SMALL_BK>, LOOP_SPREAD>;
-// 32 < T <= 64: 256 vocab x 64 tokens, 2 wavefronts, four stages of K = 64 (160 KB of LDS)
-using CfgS64 = FwdCfg<PipeCfg<2, 1, 4, LMH_S64_NS, LMH_S64_BK>, LOOP_SPREAD>;
+// T <= 64 is HBM-bound: the time is the weight stream, so these tiles are sized for streaming.
+// They cover 128 vocabulary rows (one wavefront's extent), so the 1188 tiles of V = 152064 give
+// 4.6 tiles per CU and the last round of tiles leaves few CUs idle (256-row tiles gave 2.3 per CU
+// and ran 10 % longer); one workgroup per CU holds enough loads in flight.
+// T <= 32: 128 vocab x 32 tokens, 2 wavefronts (16 tokens each), five stages of K = 64 with the
+// loads spread between the MFMAs (100 KB of LDS)
+using CfgSmall = FwdCfg<PipeCfg<LMH_SMALL_SHAPE, LMH_SMALL_NS, LMH_SMALL_BK>, LOOP_SPREAD>;
+// 32 < T <= 64: 128 vocab x 64 tokens, 4 wavefronts (16 tokens each), four stages of K = 64
+// (96 KB of LDS)
+using CfgS64 = FwdCfg<PipeCfg<LMH_S64_SHAPE, LMH_S64_NS, LMH_S64_BK>, LOOP_SPREAD>;
 
 void launch_fwd_partials(const FwdArgs& a, hipStream_t stream) {
   if (a.T <= 32)
