@@ -345,37 +345,44 @@ __device__ __forceinline__ Rec fold(Rec s, Rec r) {
   return s;
 }
 
-constexpr int FIN_TOK = 64;   // tokens per workgroup (one per lane)
 constexpr int FIN_WAVES = 16; // wavefronts per workgroup
 constexpr int FIN_NSEG = 64;  // fixed number of fold segments per row
 
-template <bool P2>
-__global__ __launch_bounds__(FIN_TOK * FIN_WAVES) void fwd_finalize_kernel(FwdArgs a, int n_c) {
-  __shared__ Rec part[FIN_NSEG][FIN_TOK];
-  constexpr int SEG_PER_WAVE = FIN_NSEG / FIN_WAVES;
-  constexpr int BATCH = 4;  // records per segment loaded before folding: 16 loads in flight
+// One workgroup folds the rows of TPW tokens (TPW = 16, 32 or 64).  Lane l of a wavefront serves
+// token l % TPW and segment slot l / TPW, so a wavefront covers 64 / TPW segments of each of its
+// tokens per pass and the 16 wavefronts cover all 64 segments in 4 TPW / 64 passes.  Small T takes
+// small TPW, so that lanes are not left idle on missing tokens; large T takes TPW = 32, which gives
+// a workgroup per CU at T = 8192.  How segments are spread over lanes does not change any value:
+// each segment is folded in ascending chunk order, then the 64 segment states in ascending order.
+template <bool P2, int TPW>
+__global__ __launch_bounds__(64 * FIN_WAVES) void fwd_finalize_kernel(FwdArgs a, int n_c) {
+  constexpr int LPT = 64 / TPW;                      // segment slots per wavefront and pass
+  constexpr int PASSES = FIN_NSEG / (FIN_WAVES * LPT);
+  constexpr int BATCH = 16 / PASSES;                 // records per segment loaded before folding
+  __shared__ Rec part[FIN_NSEG][TPW];
   const int T = a.T;
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-  const int t = blockIdx.x * FIN_TOK + lane;
+  const int tl = lane % TPW;
+  const int t = blockIdx.x * TPW + tl;
   const bool t_ok = t < T;
-  int lo[SEG_PER_WAVE], len[SEG_PER_WAVE];
-  Rec seg[SEG_PER_WAVE];
+  int sg[PASSES], lo[PASSES], len[PASSES];
+  Rec seg[PASSES];
   int maxlen = 0;
 #pragma unroll
-  for (int j = 0; j < SEG_PER_WAVE; ++j) {
-    const int s = w + FIN_WAVES * j;
-    lo[j] = (int)((int64_t)s * n_c / FIN_NSEG);
-    len[j] = (int)((int64_t)(s + 1) * n_c / FIN_NSEG) - lo[j];
+  for (int j = 0; j < PASSES; ++j) {
+    sg[j] = (j * FIN_WAVES + w) * LPT + lane / TPW;
+    lo[j] = (int)((int64_t)sg[j] * n_c / FIN_NSEG);
+    len[j] = (int)((int64_t)(sg[j] + 1) * n_c / FIN_NSEG) - lo[j];
     maxlen = max(maxlen, len[j]);
     seg[j] = Rec{-__builtin_inff(), 0.f, 0.f, 0.f, 0.f};
   }
   // Each segment is folded in ascending chunk order; the loads of a batch are all issued first.
   for (int b = 0; b < maxlen; b += BATCH) {
-    f32x4 r[SEG_PER_WAVE][BATCH];
-    float r2[SEG_PER_WAVE][BATCH];
+    f32x4 r[PASSES][BATCH];
+    float r2[PASSES][BATCH];
 #pragma unroll
-    for (int j = 0; j < SEG_PER_WAVE; ++j)
+    for (int j = 0; j < PASSES; ++j)
 #pragma unroll
       for (int i = 0; i < BATCH; ++i) {
         const int c = b + i;
@@ -385,18 +392,18 @@ __global__ __launch_bounds__(FIN_TOK * FIN_WAVES) void fwd_finalize_kernel(FwdAr
         r2[j][i] = (P2 && ok) ? a.rec2[at] : 0.f;
       }
 #pragma unroll
-    for (int j = 0; j < SEG_PER_WAVE; ++j)
+    for (int j = 0; j < PASSES; ++j)
 #pragma unroll
       for (int i = 0; i < BATCH; ++i)
         seg[j] = fold<P2>(seg[j], Rec{r[j][i][0], r[j][i][1], r[j][i][2], r[j][i][3], r2[j][i]});
   }
 #pragma unroll
-  for (int j = 0; j < SEG_PER_WAVE; ++j) part[w + FIN_WAVES * j][lane] = seg[j];
+  for (int j = 0; j < PASSES; ++j) part[sg[j]][tl] = seg[j];
   __syncthreads();
-  if (w != 0 || t >= T) return;
+  if (w != 0 || lane >= TPW || t >= T) return;
   Rec st = {-__builtin_inff(), 0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
-  for (int s = 0; s < FIN_NSEG; ++s) st = fold<P2>(st, part[s][lane]);
+  for (int s = 0; s < FIN_NSEG; ++s) st = fold<P2>(st, part[s][tl]);
 
   const float logS = logf(st.n) + log1pf(st.b / st.n);
   const int y = a.labels[t];
@@ -477,13 +484,21 @@ void launch_fwd_partials(const FwdArgs& a, hipStream_t stream) {
     launch_partials_cfg<CfgBig>(a, stream);
 }
 
+template <int TPW>
+static void launch_finalize_tpw(const FwdArgs& a, int n_c, hipStream_t stream) {
+  const int nblk = (a.T + TPW - 1) / TPW;
+  if (a.sum_p2)
+    hipLaunchKernelGGL((fwd_finalize_kernel<true, TPW>), dim3(nblk), dim3(64 * FIN_WAVES), 0, stream, a, n_c);
+  else
+    hipLaunchKernelGGL((fwd_finalize_kernel<false, TPW>), dim3(nblk), dim3(64 * FIN_WAVES), 0, stream, a, n_c);
+}
+
 void launch_fwd_finalize(const FwdArgs& a, hipStream_t stream) {
   const int n_c = (a.vocab_total + WAVE_M - 1) / WAVE_M;
-  const int nblk = (a.T + FIN_TOK - 1) / FIN_TOK;
-  if (a.sum_p2)
-    hipLaunchKernelGGL(fwd_finalize_kernel<true>, dim3(nblk), dim3(FIN_TOK * FIN_WAVES), 0, stream, a, n_c);
+  if (a.T <= 2048)
+    launch_finalize_tpw<16>(a, n_c, stream);
   else
-    hipLaunchKernelGGL(fwd_finalize_kernel<false>, dim3(nblk), dim3(FIN_TOK * FIN_WAVES), 0, stream, a, n_c);
+    launch_finalize_tpw<32>(a, n_c, stream);
 }
 
 }  // namespace lmh
