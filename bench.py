@@ -186,7 +186,7 @@ def main():
     # W (2VH bytes) streamed once for 2TVH flops: T flop/B; below the ridge the kernel is HBM-bound
     hbm_bound = T < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
     traffic = measured_traffic(a.workload)
-    kname = "fwd_partials_persistent_kernel" if T > 64 else "fwd_partials_kernel"
+    kname = "fwd_partials_persistent_kernel" if T > 128 else "fwd_partials_kernel"
     if hbm_bound:
         roof = {"bound": "hbm", "kernel": kname, "achieved": k1_gbs, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": k1_gbs / PEAK_HBM_GBS, "traffic": traffic}

@@ -46,6 +46,16 @@
 #ifndef LMH_S64_SHAPE
 #define LMH_S64_SHAPE 1, 4, 1
 #endif
+// mid-T tile (64 < T <= LMH_MID_MAX)
+#ifndef LMH_MID_MAX
+#define LMH_MID_MAX 128
+#endif
+#ifndef LMH_MID_SHAPE
+#define LMH_MID_SHAPE 2, 2, 4
+#endif
+#ifndef LMH_MID_NS
+#define LMH_MID_NS 3
+#endif
 
 namespace lmh {
 
@@ -459,10 +469,10 @@ struct FwdCfg : P {
   static constexpr int LDS_BYTES = LOOP_ == LOOP_PINGPONG ? 5 * 256 * P::ROW : P::LDS_BYTES;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
-// T > 64: 256 vocab x 256 tokens, 8 wavefronts (2 per SIMD) in two groups that alternate between
+// T > 128: 256 vocab x 256 tokens, 8 wavefronts (2 per SIMD) in two groups that alternate between
 // loads and MFMAs, K = 64 steps, three A slots and two B slots (160 KB of LDS), persistent grid.
-// From T = 96 up it beat a 4-wavefront 256 x 128 tile everywhere measured, even where most of
-// its token columns are empty: the weight stream, not the MFMA work, sets the time there.
+// Its MFMA rate is the highest of the tiles, and from T = 192 up it is the fastest even where many
+// of its token columns are empty.
 using CfgBig = FwdCfg<PipeCfg<2, 4, 4, 2, 64>, LOOP_PINGPONG>;
 // T <= 64 is HBM-bound: the time is the weight stream, so these tiles are sized for streaming.
 // They cover 128 vocabulary rows (one wavefront's extent), so the 1188 tiles of V = 152064 give
@@ -475,11 +485,17 @@ using CfgSmall = FwdCfg<PipeCfg<LMH_SMALL_SHAPE, LMH_SMALL_NS, LMH_SMALL_BK>, LO
 // (96 KB of LDS)
 using CfgS64 = FwdCfg<PipeCfg<LMH_S64_SHAPE, LMH_S64_NS, LMH_S64_BK>, LOOP_SPREAD>;
 
+// 64 < T <= 128: 256 vocab x 128 tokens, 4 wavefronts, three stages of K = 64 (144 KB of LDS).
+// Against the 256 x 256 persistent tile it wins by 13 % at T = 96 and 128 and loses from T = 192.
+using CfgMid = FwdCfg<PipeCfg<LMH_MID_SHAPE, LMH_MID_NS, 64>, LOOP_SPREAD>;
+
 void launch_fwd_partials(const FwdArgs& a, hipStream_t stream) {
   if (a.T <= 32)
     launch_partials_cfg<CfgSmall>(a, stream);
   else if (a.T <= 64)
     launch_partials_cfg<CfgS64>(a, stream);
+  else if (a.T <= LMH_MID_MAX)
+    launch_partials_cfg<CfgMid>(a, stream);
   else
     launch_partials_cfg<CfgBig>(a, stream);
 }

@@ -37,7 +37,7 @@ def test_small_workload_T64_H256_V4096():
 
 
 @pytest.mark.parametrize("T,H,V", [(1, 64, 128), (17, 136, 1000), (37, 256, 4099), (300, 520, 2053),
-                                   (513, 128, 777), (33, 64, 257)])
+                                   (513, 128, 777), (33, 64, 257), (100, 192, 3000), (128, 64, 1025)])
 def test_ragged_shapes(T, H, V):
     h, w, y = _case(T, H, V, seed=T, wstd=0.05)
     _check(h, w, y, f"ragged")

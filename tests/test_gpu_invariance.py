@@ -94,7 +94,7 @@ def test_embedded_in_2048(data, reference):
     assert mism == 0, f"{mism} rows differ bitwise inside a batch of 2048"
 
 
-@pytest.mark.parametrize("c", [1, 3, 7, 16, 32, 64])
+@pytest.mark.parametrize("c", [1, 3, 7, 16, 32, 64, 96, 128])
 def test_row_chunk_sweep(data, reference, c):
     parts = []
     for s in range(0, N_PROBE, c):
