@@ -167,10 +167,19 @@ LMH_API lmh_status_t lmhead_logprob_fwd_finalize_ex(const int32_t* labels, int64
 
 /* Backward with a temperature and an optional entropy gradient (see above); lse is the one the
  * forward wrote with the same temperature.  grad_logprob is required (pass zeros when only the
- * entropy carries a gradient). */
+ * entropy carries a gradient).
+ * Vocabulary shard: the weight rows given are the vocabulary ids [vocab_start, vocab_start + V)
+ * and lse (and entropy) are those of the whole vocabulary, as lmhead_logprob_fwd_finalize_ex
+ * writes them after all shards.  The label term is added only where the label lies in these rows
+ * (on the other shards the row keeps -p g, the out-of-range rule: SkyRL PR #1765, only the owner
+ * of a label contributes it).  grad_weight [V,H] receives the shard's rows, bitwise equal to those
+ * rows of a call on the whole weight; grad_hidden [T,H] receives this shard's share, dz[:, rows] .
+ * weight, which the caller adds over the shards (tensor-parallel: the all-reduce of grad_hidden).
+ * vocab_start = 0 is the whole vocabulary.  vocab_start < 0 or vocab_start + V >= 2^31 gives
+ * LMH_ERR_INVALID_ARG. */
 LMH_API lmh_status_t lmhead_logprob_bwd_ex(const void* hidden, const void* weight, const int32_t* labels,
                                            int64_t T, int64_t H, int64_t V, float temperature,
-                                           const float* grad_logprob, const float* lse,
+                                           int64_t vocab_start, const float* grad_logprob, const float* lse,
                                            const float* grad_entropy, const float* entropy,
                                            float* grad_hidden, float* grad_weight, int accumulate_grad_weight,
                                            void* workspace, size_t workspace_bytes, hipStream_t stream);

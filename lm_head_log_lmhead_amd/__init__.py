@@ -40,7 +40,8 @@ _SIGNATURES = {
     "lmhead_logprob_fwd_ex": (_INT, [_P, _P, _P, _I64, _I64, _I64, _F, _P, _P, _P, _P, _P, _SZ, _P]),
     "lmhead_logprob_fwd_partials_ex": (_INT, [_P, _P, _P, _I64, _I64, _I64, _F, _I64, _I64, _INT, _P, _SZ, _P]),
     "lmhead_logprob_fwd_finalize_ex": (_INT, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _SZ, _P]),
-    "lmhead_logprob_bwd_ex": (_INT, [_P, _P, _P, _I64, _I64, _I64, _F, _P, _P, _P, _P, _P, _P, _INT, _P, _SZ, _P]),
+    "lmhead_logprob_bwd_ex": (_INT, [_P, _P, _P, _I64, _I64, _I64, _F, _I64, _P, _P, _P, _P, _P, _P, _INT, _P, _SZ,
+                                     _P]),
     "lmhead_status_string": (ctypes.c_char_p, [_INT]),
 }
 
@@ -209,7 +210,7 @@ def lmhead_logprob_fwd_finalize_ex(labels, T, H, V, logprob, entropy=None, lse=N
 
 def lmhead_logprob_bwd_ex(hidden, weight, labels, temperature: float, grad_logprob, lse, grad_entropy=None,
                           entropy=None, grad_hidden=None, grad_weight=None, accumulate_grad_weight: bool = False,
-                          workspace=None, stream=None) -> None:
+                          workspace=None, stream=None, vocab_start: int = 0) -> None:
     T, H, V = _dims(hidden, weight)
     _check_tensor(hidden, "hidden", torch.bfloat16)
     _check_tensor(weight, "weight", torch.bfloat16)
@@ -219,7 +220,7 @@ def lmhead_logprob_bwd_ex(hidden, weight, labels, temperature: float, grad_logpr
     _check_tensor(grad_hidden, "grad_hidden", torch.float32, T * H)
     _check_tensor(grad_weight, "grad_weight", torch.float32, V * H)
     _check(lib().lmhead_logprob_bwd_ex(_ptr(hidden), _ptr(weight), _ptr(labels), T, H, V, float(temperature),
-                                       _ptr(grad_logprob), _ptr(lse), _ptr(grad_entropy), _ptr(entropy),
+                                       int(vocab_start), _ptr(grad_logprob), _ptr(lse), _ptr(grad_entropy), _ptr(entropy),
                                        _ptr(grad_hidden), _ptr(grad_weight), int(bool(accumulate_grad_weight)),
                                        _ptr(workspace), _nbytes(workspace), _stream(stream)), "lmhead_logprob_bwd_ex")
 
@@ -255,19 +256,19 @@ def forward(hidden: torch.Tensor, weight: torch.Tensor, labels: torch.Tensor, en
 
 
 def backward(hidden, weight, labels, grad_logprob, lse, need_hidden=True, need_weight=True, stream=None,
-             temperature: float = 1.0, grad_entropy=None, entropy=None):
+             temperature: float = 1.0, grad_entropy=None, entropy=None, vocab_start: int = 0):
     """Allocate gradients and workspace with torch and run lmhead_logprob_bwd (overwrite mode;
-    lmhead_logprob_bwd_ex when a temperature or an entropy gradient is given)."""
+    lmhead_logprob_bwd_ex when a temperature, an entropy gradient or a vocabulary shard is given)."""
     T, H, V = _dims(hidden, weight)
     dev = hidden.device
     gh = torch.empty((T, H), dtype=torch.float32, device=dev) if need_hidden else None
     gw = torch.empty((V, H), dtype=torch.float32, device=dev) if need_weight else None
     ws = _workspace(lmhead_logprob_bwd_workspace_size(T, H, V), dev)
-    if temperature == 1.0 and grad_entropy is None:
+    if temperature == 1.0 and grad_entropy is None and vocab_start == 0:
         lmhead_logprob_bwd(hidden, weight, labels, grad_logprob, lse, gh, gw, False, ws, stream)
     else:
         lmhead_logprob_bwd_ex(hidden, weight, labels, temperature, grad_logprob, lse, grad_entropy, entropy, gh, gw,
-                              False, ws, stream)
+                              False, ws, stream, vocab_start)
     return gh, gw
 
 

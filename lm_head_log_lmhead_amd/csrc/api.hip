@@ -188,12 +188,13 @@ lmh_status_t fwd_impl(const void* hidden, const void* weight, const int32_t* lab
 }
 
 lmh_status_t bwd_impl(const void* hidden, const void* weight, const int32_t* labels, int64_t T, int64_t H, int64_t V,
-                      float temperature, const float* grad_logprob, const float* lse, const float* grad_entropy,
+                      float temperature, int64_t vocab_start, const float* grad_logprob, const float* lse, const float* grad_entropy,
                       const float* entropy, float* grad_hidden, float* grad_weight, int accumulate_grad_weight,
                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
   LMH_TRY(check_sizes(T, H, V));
   if (accumulate_grad_weight != 0 && accumulate_grad_weight != 1) return LMH_ERR_INVALID_ARG;
   LMH_TRY(check_temperature(temperature));
+  if (vocab_start < 0 || vocab_start > MAX_V - V) return LMH_ERR_INVALID_ARG;
   if (T >= MAX_T_BWD) return LMH_ERR_UNSUPPORTED;
   if (T == 0) return LMH_OK;  // no rows: nothing is launched and the gradient buffers are untouched
   LMH_TRY(check_inputs(hidden, weight, labels));
@@ -219,6 +220,7 @@ lmh_status_t bwd_impl(const void* hidden, const void* weight, const int32_t* lab
   a.grad_entropy = grad_entropy;
   a.entropy = grad_entropy ? entropy : nullptr;
   a.temperature = temperature;
+  a.vocab_start = (int)vocab_start;
   a.grad_hidden = grad_hidden;
   a.grad_weight = grad_weight;
   a.accumulate_gw = accumulate_grad_weight;
@@ -287,17 +289,18 @@ lmh_status_t lmhead_logprob_bwd(const void* hidden, const void* weight, const in
                                 int64_t V, const float* grad_logprob, const float* lse, float* grad_hidden,
                                 float* grad_weight, int accumulate_grad_weight, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream) {
-  return bwd_impl(hidden, weight, labels, T, H, V, 1.0f, grad_logprob, lse, nullptr, nullptr, grad_hidden,
+  return bwd_impl(hidden, weight, labels, T, H, V, 1.0f, 0, grad_logprob, lse, nullptr, nullptr, grad_hidden,
                   grad_weight, accumulate_grad_weight, workspace, workspace_bytes, stream);
 }
 
 lmh_status_t lmhead_logprob_bwd_ex(const void* hidden, const void* weight, const int32_t* labels, int64_t T,
-                                   int64_t H, int64_t V, float temperature, const float* grad_logprob,
-                                   const float* lse, const float* grad_entropy, const float* entropy,
-                                   float* grad_hidden, float* grad_weight, int accumulate_grad_weight,
-                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return bwd_impl(hidden, weight, labels, T, H, V, temperature, grad_logprob, lse, grad_entropy, entropy, grad_hidden,
-                  grad_weight, accumulate_grad_weight, workspace, workspace_bytes, stream);
+                                   int64_t H, int64_t V, float temperature, int64_t vocab_start,
+                                   const float* grad_logprob, const float* lse, const float* grad_entropy,
+                                   const float* entropy, float* grad_hidden, float* grad_weight,
+                                   int accumulate_grad_weight, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream) {
+  return bwd_impl(hidden, weight, labels, T, H, V, temperature, vocab_start, grad_logprob, lse, grad_entropy, entropy,
+                  grad_hidden, grad_weight, accumulate_grad_weight, workspace, workspace_bytes, stream);
 }
 
 const char* lmhead_status_string(lmh_status_t s) {

@@ -36,8 +36,8 @@ template <class Cfg, bool SCALED, bool EGRAD>
 __global__ __launch_bounds__(Cfg::NTHREADS) void bwd_dz_kernel(
     const __bf16* __restrict__ hidden, const __bf16* __restrict__ weight, const int* __restrict__ labels,
     const float* __restrict__ grad, const float* __restrict__ lse, const float* __restrict__ grad_entropy,
-    const float* __restrict__ entropy, float temperature, int T, int H, int V, int vs0, int Vc, int Vs, int n_mt,
-    int n_nt, __bf16* __restrict__ dz, __bf16* __restrict__ dzt, int ldt) {
+    const float* __restrict__ entropy, float temperature, int T, int H, int V, int vocab_start, int vs0, int Vc,
+    int Vs, int n_mt, int n_nt, __bf16* __restrict__ dz, __bf16* __restrict__ dzt, int ldt) {
   loop_placement_pad<4 + 2 * SCALED + EGRAD>();
   constexpr int STAGE_OUT = Cfg::NWAVES * Cfg::WAVE_N * DZ_PITCH;
   constexpr int LDS = PingPong<Cfg>::LDS_BYTES > STAGE_OUT ? PingPong<Cfg>::LDS_BYTES : STAGE_OUT;
@@ -71,7 +71,9 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void bwd_dz_kernel(
     const bool tok_ok = tok < T;
     float g = tok_ok ? grad[tok] : 0.f;
     const float L = tok_ok ? lse[tok] : 0.f;
-    const int y = tok_ok ? labels[tok] : -1;
+    // the label as a weight row of this call (-1 when another shard's or out of range)
+    const int yg = tok_ok ? labels[tok] : -1;
+    const int y = yg >= vocab_start && yg - vocab_start < V ? yg - vocab_start : -1;
     float ge = 0.f, He = 0.f;
     if (EGRAD) {
       ge = tok_ok ? grad_entropy[tok] : 0.f;
@@ -417,7 +419,8 @@ void launch_bwd(const BwdArgs& a, hipStream_t stream) {
       auto kern = scaled ? (egrad ? bwd_dz_kernel<CfgDz, true, true> : bwd_dz_kernel<CfgDz, true, false>)
                          : (egrad ? bwd_dz_kernel<CfgDz, false, true> : bwd_dz_kernel<CfgDz, false, false>);
       hipLaunchKernelGGL(kern, dim3(n_mt * n_nt), dim3(CfgDz::NTHREADS), 0, stream, a.hidden, a.weight, a.labels,
-                         a.grad, a.lse, a.grad_entropy, a.entropy, a.temperature, L.T, L.H, L.V, vs0, Vc, L.Vs, n_mt,
+                         a.grad, a.lse, a.grad_entropy, a.entropy, a.temperature, L.T, L.H, L.V, a.vocab_start, vs0,
+                         Vc, L.Vs, n_mt,
                          n_nt, dz, dzt, L.Tp);
     }
     // dz^T rows hold tokens up to T rounded up to 8 (zeros past T); the gradient GEMM reads no

@@ -61,6 +61,7 @@ struct BwdArgs {
   const float* grad_entropy;  // [T] upstream gradient of the entropies, or null
   const float* entropy;       // [T] forward entropies (needed with grad_entropy)
   float temperature;
+  int vocab_start;            // vocabulary id of weight row 0 (labels are vocabulary ids)
   float* grad_hidden;
   float* grad_weight;
   int accumulate_gw;

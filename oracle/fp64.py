@@ -49,7 +49,8 @@ peaked-row closed form of the entropy; central finite differences of the backwar
 closed form of both gradients; the column sums of ``grad_weight``; with a temperature, the
 one-hot, two-entry and infinite-temperature closed forms and finite differences; for
 ``sum_p2``, the one-hot and uniform closed forms; for the entropy gradient, finite differences of
-the entropy.  No function here is unpinned.
+the entropy; for a vocabulary shard's share of the backward, that the shares of a partition add
+up to the whole backward.  No function here is unpinned.
 """
 from __future__ import annotations
 
@@ -184,6 +185,33 @@ def backward(hidden, weight, labels, grad, row_block: int = DEFAULT_ROW_BLOCK, t
         _, _, logp = _block_softmax_terms(h[sl], W, tau)
         dz = _dz_block(logp, y[sl], g[sl], V, tau, None if ge is None else ge[sl])
         gh[sl] = dz @ W
+        gW += dz.T @ h[sl]
+    return gh, gW
+
+
+def backward_shard(hidden, weight, labels, grad, v0: int, v1: int, row_block: int = DEFAULT_ROW_BLOCK,
+                   temperature=1.0, grad_entropy=None):
+    """The share of the vocabulary rows [v0, v1) in the gradients, the softmax being over the
+    whole vocabulary: returns (dz[:, v0:v1] @ W[v0:v1], grad_weight rows v0 .. v1-1).  The label
+    term appears only in the shard that holds the label (SkyRL PR #1765, design commit: in the
+    vocabulary-parallel path only the owner of a target contributes it).  By linearity the shares
+    of a partition of the vocabulary add up to ``backward``."""
+    h = to_f64(hidden)
+    W = to_f64(weight)
+    y = _labels(labels)
+    g = to_f64(grad)
+    ge = None if grad_entropy is None else to_f64(grad_entropy)
+    tau = _temperature(temperature)
+    T, V = h.shape[0], W.shape[0]
+    if not 0 <= v0 <= v1 <= V:
+        raise ValueError(f"shard [{v0}, {v1}) outside the vocabulary of {V}")
+    gh = np.zeros_like(h)
+    gW = np.zeros((v1 - v0, h.shape[1]))
+    for s in range(0, T, row_block):
+        sl = slice(s, min(T, s + row_block))
+        _, _, logp = _block_softmax_terms(h[sl], W, tau)
+        dz = _dz_block(logp, y[sl], g[sl], V, tau, None if ge is None else ge[sl])[:, v0:v1]
+        gh[sl] = dz @ W[v0:v1]
         gW += dz.T @ h[sl]
     return gh, gW
 

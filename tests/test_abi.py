@@ -147,14 +147,19 @@ def test_extended_entry_validation_codes(lib):
         lmh.LMH_ERR_UNSUPPORTED
 
     def bwd_ex(temp=1.0, **kw):
-        a = dict(h=16, w=16, y=16, T=4, H=8, V=10, g=16, lse=16, ge=None, ent=None, gh=16, gw=16, acc=0, ws=256,
-                 wsb=1 << 30)
+        a = dict(h=16, w=16, y=16, T=4, H=8, V=10, vs=0, g=16, lse=16, ge=None, ent=None, gh=16, gw=16, acc=0,
+                 ws=256, wsb=1 << 30)
         a.update(kw)
-        return lib.lmhead_logprob_bwd_ex(a["h"], a["w"], a["y"], a["T"], a["H"], a["V"], temp, a["g"], a["lse"],
-                                         a["ge"], a["ent"], a["gh"], a["gw"], a["acc"], a["ws"], a["wsb"], None)
+        return lib.lmhead_logprob_bwd_ex(a["h"], a["w"], a["y"], a["T"], a["H"], a["V"], temp, a["vs"], a["g"],
+                                         a["lse"], a["ge"], a["ent"], a["gh"], a["gw"], a["acc"], a["ws"], a["wsb"],
+                                         None)
 
     assert bwd_ex(0.0) == lmh.LMH_ERR_INVALID_ARG
     assert bwd_ex(1.0, ge=16) == lmh.LMH_ERR_INVALID_ARG            # entropy gradient without the entropy
     assert bwd_ex(1.0, ge=16, ent=6) == lmh.LMH_ERR_UNSUPPORTED
     assert bwd_ex(1.3, wsb=64) == lmh.LMH_ERR_WORKSPACE_TOO_SMALL
     assert bwd_ex(1.3, gh=None, gw=None, ge=16, ent=16) == lmh.LMH_OK
+    assert bwd_ex(1.0, vs=-128) == lmh.LMH_ERR_INVALID_ARG           # vocabulary shard before id 0
+    assert bwd_ex(1.0, vs=2**31 - 10) == lmh.LMH_ERR_INVALID_ARG     # shard past the 31-bit id range
+    assert bwd_ex(1.0, vs=2**31 - 11, gh=None, gw=None) == lmh.LMH_OK
+    assert bwd_ex(1.0, vs=77, gh=None, gw=None) == lmh.LMH_OK        # any start: no records are written

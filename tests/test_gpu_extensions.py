@@ -153,6 +153,38 @@ def test_backward_with_temperature_and_entropy_gradient(T, H, V, tau, egrad):
     assert e1 <= GRAD_REL_FRO and e2 <= GRAD_REL_FRO
 
 
+@pytest.mark.parametrize("tau,egrad", [(1.0, False), (0.7, True)])
+def test_backward_vocabulary_shards(tau, egrad):
+    # Shards of the weight with the whole vocabulary's lse: each shard's grad_weight rows are the
+    # bits of the whole call's rows, the grad_hidden shares add up to the whole call's, and every
+    # share matches the oracle's share.  Shard starts need no alignment in the backward.
+    tau = f32(tau)
+    T, H, V = 100, 192, 3000
+    print(f"[case] bwd_ex shards T={T} H={H} V={V} tau={tau} entropy_grad={egrad}", flush=True)
+    h, w, y, g = _case(T, H, V, seed=31)
+    y = y.clone()
+    y[:3] = torch.tensor([5, 1500, 2999], dtype=y.dtype)
+    y[3] = -100
+    ge = synth.upstream_grad(T, 32) if egrad else None
+    hd, wd, yd, gd = to_dev(h, w, y, g)
+    ged = None if ge is None else ge.to(dev())
+    _, ent, lse = lmh.forward(hd, wd, yd, entropy=True, want_lse=True, temperature=tau)
+    gh, gw = lmh.backward(hd, wd, yd, gd, lse, temperature=tau, grad_entropy=ged, entropy=ent, vocab_start=0)
+    bounds = [0, 1000, 1501, 2990, V]
+    gh_sum = torch.zeros_like(gh)
+    for v0, v1 in zip(bounds[:-1], bounds[1:]):
+        ghs, gws = lmh.backward(hd, wd[v0:v1], yd, gd, lse, temperature=tau, grad_entropy=ged, entropy=ent,
+                                vocab_start=v0)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(gws), bits(gw[v0:v1])), f"grad_weight rows of shard [{v0}, {v1})"
+        rgh, rgw = fp64.backward_shard(h, w, y, g, v0, v1, temperature=tau, grad_entropy=ge)
+        e1, e2 = rel_fro(_np(ghs), rgh), rel_fro(_np(gws), rgw)
+        print(f"shard [{v0}, {v1}) rel fro grad_hidden {e1:.3e} grad_weight {e2:.3e}", flush=True)
+        assert e1 <= GRAD_REL_FRO and e2 <= GRAD_REL_FRO
+        gh_sum += ghs
+    assert rel_fro(_np(gh_sum), _np(gh)) <= 1e-5
+
+
 def test_entropy_only_gradient():
     # only the entropy carries a gradient: zero upstream gradient on the log-probs
     T, H, V = 64, 128, 2053

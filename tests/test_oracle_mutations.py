@@ -5,6 +5,7 @@ Each mutant replaces one internal step of ``oracle.fp64`` via monkeypatch; the p
 """
 import numpy as np
 import pytest
+import torch
 
 from oracle import fp64
 from tests import test_oracle_pins as pins
@@ -80,6 +81,28 @@ def _sum_p_not_squared(p):
     return p.sum(axis=1)
 
 
+_shard_right = fp64.backward_shard
+
+
+def _shard_local_softmax(hidden, weight, labels, grad, v0, v1, row_block=128, temperature=1.0, grad_entropy=None):
+    # the softmax taken over the shard's own rows instead of the whole vocabulary
+    y = fp64._labels(labels) - v0
+    y[(y < 0) | (y >= v1 - v0)] = -1
+    gh, gw = fp64.backward(hidden, weight[v0:v1], torch.as_tensor(y), grad, row_block, temperature, grad_entropy)
+    return gh, gw
+
+
+def _shard_label_everywhere(hidden, weight, labels, grad, v0, v1, row_block=128, temperature=1.0, grad_entropy=None):
+    # every shard adds the label term (it belongs to the owner only)
+    gh, gw = _shard_right(hidden, weight, labels, grad, v0, v1, row_block, temperature, grad_entropy)
+    y = fp64._labels(labels)
+    W = fp64.to_f64(weight)
+    g = fp64.to_f64(grad)
+    r = np.nonzero((y >= 0) & (y < W.shape[0]) & ((y < v0) | (y >= v1)))[0]
+    gh[r] += (g[r] / float(temperature))[:, None] * W[y[r]]
+    return gh, gw
+
+
 PIN_SETS = {
     "forward": [
         lambda: pins.test_fp64_matches_brute_forward(5, 24, 7),
@@ -104,6 +127,10 @@ PIN_SETS = {
         pins.test_fp64_matches_brute_backward_temperature_and_entropy_grad,
         lambda: pins.test_backward_with_temperature_and_entropy_matches_central_differences(0.6, False),
         lambda: pins.test_backward_with_temperature_and_entropy_matches_central_differences(2.2, True),
+    ],
+    "shards": [
+        lambda: pins.test_backward_shards_add_up_to_the_whole(1.0, False),
+        lambda: pins.test_backward_shards_add_up_to_the_whole(0.8, True),
     ],
     "sum_p2": [
         lambda: pins.test_fp64_matches_brute_with_temperature(4, 24, 7, 0.7),
@@ -133,6 +160,8 @@ def _some_pin_fails(kind):
     ("entropy gradient sign", "_dz_block", _dz_entropy_sign, "backward_ext"),
     ("entropy gradient without the entropy term", "_dz_block", _dz_entropy_no_h, "backward_ext"),
     ("sum_p2 not squared", "_sum_p2", _sum_p_not_squared, "sum_p2"),
+    ("shard softmax over its own rows", "backward_shard", _shard_local_softmax, "shards"),
+    ("label term in every shard", "backward_shard", _shard_label_everywhere, "shards"),
 ])
 def test_pins_catch_planted_mistake(monkeypatch, name, target, mutant, kind):
     monkeypatch.setattr(fp64, target, mutant)

@@ -234,6 +234,36 @@ def test_grad_weight_column_sums():
     np.testing.assert_allclose(gW.sum(axis=0), expect, atol=1e-12, rtol=0)
 
 
+@pytest.mark.parametrize("tau,with_ge", [(1.0, False), (0.8, True)])
+def test_backward_shards_add_up_to_the_whole(tau, with_ge):
+    # Linearity: the shares of a partition of the vocabulary sum to the whole backward, and the
+    # grad_weight rows are the whole backward's rows (labels in every shard, one out of range).
+    T, H, V = 9, 10, 11
+    h, W, y = _rand_case(T, H, V, seed=41)
+    y = y.clone()
+    y[:4] = torch.tensor([0, 4, 8, 10], dtype=y.dtype)
+    y[4] = -100
+    g = synth.upstream_grad(T, 41)
+    ge = synth.upstream_grad(T, 42) if with_ge else None
+    gh, gW = fp64.backward(h, W, y, g, temperature=tau, grad_entropy=ge)
+    bounds = [0, 3, 4, 8, V]
+    shares = [fp64.backward_shard(h, W, y, g, a, b, temperature=tau, grad_entropy=ge)
+              for a, b in zip(bounds[:-1], bounds[1:])]
+    np.testing.assert_allclose(sum(s[0] for s in shares), gh, rtol=0, atol=1e-12 * np.abs(gh).max())
+    np.testing.assert_allclose(np.concatenate([s[1] for s in shares]), gW, rtol=0, atol=1e-12 * np.abs(gW).max())
+    # a shard without any of the labels has no label term: its share is -g sum_v p_v W_v (tau = 1,
+    # no entropy gradient), checked against the brute-force probabilities
+    if not with_ge:
+        yb = y.clone()
+        yb[:] = 0
+        gh1, _ = fp64.backward_shard(h, W, yb, g, 5, V)
+        z = fp64.to_f64(h) @ fp64.to_f64(W).T
+        p = np.exp(z - z.max(1, keepdims=True))
+        p /= p.sum(1, keepdims=True)
+        expect = -fp64.to_f64(g)[:, None] * (p[:, 5:] @ fp64.to_f64(W)[5:])
+        np.testing.assert_allclose(gh1, expect, rtol=0, atol=1e-12 * np.abs(expect).max())
+
+
 # --------------------------------------------------------------------------------------------
 # temperature, sum of squared probabilities, entropy gradient
 # --------------------------------------------------------------------------------------------
