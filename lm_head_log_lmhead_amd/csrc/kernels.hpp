@@ -14,7 +14,10 @@ constexpr int VOCAB_CHUNK = WAVE_M;
 // Vocabulary rows per backward step (a multiple of the 256-row tile and of the K step).
 // grad_hidden does not depend on it bit-wise: each step continues the previous step's MFMA
 // accumulation chain.
-constexpr int BWD_VOCAB_STEP = 16384;
+#ifndef LMH_BWD_STEP
+#define LMH_BWD_STEP 65536
+#endif
+constexpr int BWD_VOCAB_STEP = LMH_BWD_STEP;
 
 // Words of the forward workspace used by the large-T tile scheduler (one counter per XCD).
 constexpr int SCHED_WORDS = 16;
