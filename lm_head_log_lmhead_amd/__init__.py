@@ -220,8 +220,9 @@ def lmhead_logprob_bwd_ex(hidden, weight, labels, temperature: float, grad_logpr
     _check_tensor(grad_hidden, "grad_hidden", torch.float32, T * H)
     _check_tensor(grad_weight, "grad_weight", torch.float32, V * H)
     _check(lib().lmhead_logprob_bwd_ex(_ptr(hidden), _ptr(weight), _ptr(labels), T, H, V, float(temperature),
-                                       int(vocab_start), _ptr(grad_logprob), _ptr(lse), _ptr(grad_entropy), _ptr(entropy),
-                                       _ptr(grad_hidden), _ptr(grad_weight), int(bool(accumulate_grad_weight)),
+                                       int(vocab_start), _ptr(grad_logprob), _ptr(lse), _ptr(grad_entropy),
+                                       _ptr(entropy), _ptr(grad_hidden), _ptr(grad_weight),
+                                       int(bool(accumulate_grad_weight)),
                                        _ptr(workspace), _nbytes(workspace), _stream(stream)), "lmhead_logprob_bwd_ex")
 
 

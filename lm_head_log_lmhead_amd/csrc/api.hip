@@ -118,12 +118,11 @@ FwdArgs make_fwd_args(const void* hidden, const void* weight, const int32_t* lab
 
 // The weight rows of a call are the vocabulary ids [vocab_start, vocab_start + V) of a
 // vocabulary of vocab_total; shards start on a chunk and all but the last cover whole chunks.
-lmh_status_t check_shard(int64_t H, int64_t V, int64_t vocab_start, int64_t vocab_total) {
+lmh_status_t check_shard(int64_t V, int64_t vocab_start, int64_t vocab_total) {
   if (V <= 0 || vocab_start < 0 || vocab_total <= 0) return LMH_ERR_INVALID_ARG;
   if (vocab_start + V > vocab_total) return LMH_ERR_INVALID_ARG;
   if (vocab_start % lmh::VOCAB_CHUNK != 0) return LMH_ERR_UNSUPPORTED;
   if (V % lmh::VOCAB_CHUNK != 0 && vocab_start + V != vocab_total) return LMH_ERR_UNSUPPORTED;
-  (void)H;
   return LMH_OK;
 }
 
@@ -131,7 +130,7 @@ lmh_status_t fwd_partials_impl(const void* hidden, const void* weight, const int
                                int64_t V, float temperature, int64_t vocab_start, int64_t vocab_total,
                                int want_sum_p2, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   LMH_TRY(check_sizes(T, H, vocab_total));
-  LMH_TRY(check_shard(H, V, vocab_start, vocab_total));
+  LMH_TRY(check_shard(V, vocab_start, vocab_total));
   if (want_sum_p2 != 0 && want_sum_p2 != 1) return LMH_ERR_INVALID_ARG;
   LMH_TRY(check_temperature(temperature));
   if (T == 0) return LMH_OK;
@@ -188,9 +187,9 @@ lmh_status_t fwd_impl(const void* hidden, const void* weight, const int32_t* lab
 }
 
 lmh_status_t bwd_impl(const void* hidden, const void* weight, const int32_t* labels, int64_t T, int64_t H, int64_t V,
-                      float temperature, int64_t vocab_start, const float* grad_logprob, const float* lse, const float* grad_entropy,
-                      const float* entropy, float* grad_hidden, float* grad_weight, int accumulate_grad_weight,
-                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                      float temperature, int64_t vocab_start, const float* grad_logprob, const float* lse,
+                      const float* grad_entropy, const float* entropy, float* grad_hidden, float* grad_weight,
+                      int accumulate_grad_weight, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   LMH_TRY(check_sizes(T, H, V));
   if (accumulate_grad_weight != 0 && accumulate_grad_weight != 1) return LMH_ERR_INVALID_ARG;
   LMH_TRY(check_temperature(temperature));

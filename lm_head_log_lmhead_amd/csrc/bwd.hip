@@ -3,9 +3,11 @@
 // The backward of sum_t g_t * logprob_t recomputes the logits instead of keeping them (SkyRL PR
 // #1765 "[megatron] Triton backend for fused LM-head log-prob", design commit: per-chunk logits
 // are recomputed in backward) and uses dz_tj = g_t * ([j == y_t] - p_tj) with p = exp(z - lse);
-// a label outside [0, V) contributes no label term, so dz = -g * p there (same PR,
-// precision-policy commit; streaming-backward commit: exp of the log-softmax, negated, times the
-// upstream gradient, plus the upstream gradient at the label).
+// a label outside the call's weight rows contributes no label term, so dz = -g * p there (same
+// PR, precision-policy commit; streaming-backward commit: exp of the log-softmax, negated, times
+// the upstream gradient, plus the upstream gradient at the label).  The rows are the vocabulary
+// ids [vocab_start, vocab_start + V): with vocab_start > 0 the call is one shard of a larger
+// vocabulary, lse is the whole vocabulary's, and only the shard holding a label adds its term.
 //
 // The vocabulary is walked in fixed steps of Vs rows.  Per step:
 //   K3 bwd_dz     : logit tile recompute (same MFMA main loop and tiles as the forward) and
