@@ -44,8 +44,9 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="fwd_T8192_H4096_V152064_peaked", choices=sorted(synth.WORKLOADS))
-    p.add_argument("--cpu-sample-rows", type=int, default=256,
-                   help="rows of the workload the CPU oracle is timed on (0 disables the CPU baseline)")
+    p.add_argument("--cpu-sample-rows", type=int, default=-1,
+                   help="rows of the workload the CPU oracle is timed on (0 disables the CPU baseline; "
+                        "-1 sizes the sample to about CPU_TARGET_S seconds of oracle work)")
     p.add_argument("--copy-bytes", type=int, default=0,
                    help="also run a plain device copy of this many bytes (counter calibration)")
     return p.parse_args()
@@ -73,17 +74,30 @@ def measured_traffic(workload: str):
     return float(t.group(1))
 
 
+CPU_TARGET_S = 15.0     # seconds of oracle work the automatic CPU sample aims at
+CPU_PROBE_ROWS = 128    # rows timed first to size the automatic sample
+
+
 def cpu_baseline(x, rows: int, name: str, temperature: float = 1.0, sum_p2: bool = False):
-    """Times the fp64 CPU oracle (as it stands) on the first `rows` rows of the same inputs."""
+    """Times the fp64 CPU oracle (as it stands) on the first `rows` rows of the same inputs; with
+    rows < 0 the sample is sized from a short probe to about CPU_TARGET_S seconds (whole multiples
+    of the probe, at most every row)."""
     from oracle import fp64
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:
         cores = os.cpu_count()
+    T = x.hidden.shape[0]
+    W = fp64.to_f64(x.weight)          # conversion is outside the timed region
+    if rows < 0:
+        probe = min(CPU_PROBE_ROWS, T)
+        t0 = time.perf_counter()
+        fp64.forward(x.hidden[:probe], W, x.labels[:probe], entropy=True, temperature=temperature, sum_p2=sum_p2)
+        per_row = (time.perf_counter() - t0) / probe
+        rows = int(min(T, max(probe, probe * round(CPU_TARGET_S / per_row / probe))))
     h = x.hidden[:rows]
     y = x.labels[:rows]
-    W = fp64.to_f64(x.weight)          # conversion is outside the timed region
     t0 = time.perf_counter()
     fp64.forward(h, W, y, entropy=True, temperature=temperature, sum_p2=sum_p2)
     dt = time.perf_counter() - t0
@@ -220,8 +234,9 @@ def main():
     }
     if wl.backward:
         out["bwd_tflops"] = 6.0 * T * H * V / (kb * 1e-3) / 1e12
-    if a.cpu_sample_rows > 0:
-        print(f"[bench] timing the CPU oracle on {a.cpu_sample_rows} rows", file=sys.stderr, flush=True)
+    if a.cpu_sample_rows != 0:
+        print(f"[bench] timing the CPU oracle ({'automatic sample' if a.cpu_sample_rows < 0 else a.cpu_sample_rows} "
+              "rows)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(x, min(a.cpu_sample_rows, T), a.workload, tau, wl.sum_p2)
     print(json.dumps(out), flush=True)
 
