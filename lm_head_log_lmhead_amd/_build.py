@@ -79,10 +79,15 @@ def _tool(name: str):
 
 
 def _loop_offsets(elf: str) -> dict[int, int]:
-    """Byte address of the K-loop head of every padded kernel in a device code object: the
-    target of the first backward branch after the kernel's first run of 64 MFMAs."""
+    """Byte address of the K-loop head of every padded kernel in a device code object."""
     out = subprocess.run([_tool("llvm-objdump"), "-d", "--no-show-raw-insn", elf], capture_output=True,
                          text=True, check=True).stdout.splitlines()
+    return loop_heads(out)
+
+
+def loop_heads(out: list[str]) -> dict[int, int]:
+    """From llvm-objdump -d lines: per padded kernel, the target of the first backward branch
+    after the kernel's first run of 64 MFMAs (the head of its K loop)."""
     heads = [i for i, l in enumerate(out) if re.match(r"^[0-9a-f]+ <", l)]
     found = {}
     for k, st in enumerate(heads):
@@ -126,6 +131,15 @@ def _measure(defines: list[str]) -> dict[int, int]:
         return found
 
 
+def pads_for(at: dict[int, int]) -> list[int]:
+    """4-byte no-op counts that move each loop head at byte address at[kid] to LOOP_TARGET modulo
+    LOOP_GRANULE (the pad sits before the loop, so it shifts the head by 4 bytes per no-op)."""
+    pads = [0] * N_LOOP_KERNELS
+    for kid, addr in at.items():
+        pads[kid] = ((LOOP_TARGET - addr) % LOOP_GRANULE) // 4
+    return pads
+
+
 def loop_pads(verbose: bool = False):
     """No-op counts that put every padded kernel's K loop at LOOP_TARGET (None if not measurable)."""
     if not (_tool("llvm-objdump") and _tool("clang-offload-bundler")):
@@ -136,9 +150,7 @@ def loop_pads(verbose: bool = False):
         if verbose:
             print(f"loop placement not measured: {e}", file=sys.stderr)
         return None
-    pads = [0] * N_LOOP_KERNELS
-    for kid, addr in at.items():
-        pads[kid] = ((LOOP_TARGET - addr) % LOOP_GRANULE) // 4
+    pads = pads_for(at)
     if verbose:
         print(f"loop heads {dict(sorted((k, hex(a)) for k, a in at.items()))} -> pads {pads}", flush=True)
     return pads
