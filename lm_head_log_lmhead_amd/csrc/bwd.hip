@@ -322,6 +322,13 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void gemm_tn_f32_persistent_kernel(G
   for (;;) {
     f32x4 acc[MSUB][Cfg::NSUB];
     gemm_acc_init<Cfg>(second ? p1 : p0, m0, n0, acc);
+    // The accumulators are complete here (their loads waited for).  Without this the compiler
+    // waits for them at their first MFMA inside the K loop, and those vmcnt waits, executed on
+    // every step, also wait for the prefetching loads the step has just issued (5 % of the GEMM).
+#pragma unroll
+    for (int m = 0; m < MSUB; ++m)
+#pragma unroll
+      for (int n = 0; n < Cfg::NSUB; ++n) asm volatile("" : "+v"(acc[m][n]));
     pp.run(acc);
     if (threadIdx.x == 0) bc[0] = q.resolve(xcd, claim);
     __syncthreads();
