@@ -288,9 +288,13 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void fwd_partials_persistent_kernel(
       for (int n = 0; n < Cfg::NSUB; ++n) acc[m][n] = (f32x4)(0.0f);
     pp.run(acc);
     // The labels are consumed here, before the next tile's loads go out: the compiler's wait for
-    // them then covers nothing else.
+    // them then covers nothing else.  The empty asm pins the offsets here; left free, the compiler
+    // sank them below the next tile's loads, and its wait for the labels then also waited for
+    // those loads before the records could start.
     int lw[Cfg::NSUB];
     label_offsets(y, v0 + wm * WAVE_M, a, lw);
+#pragma unroll
+    for (int n = 0; n < Cfg::NSUB; ++n) asm volatile("" : "+v"(lw[n]));
     if (threadIdx.x == 0) bc[0] = q.resolve(xcd, claim);
     __syncthreads();
     const int Ln = bc[0];
