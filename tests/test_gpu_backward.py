@@ -23,7 +23,9 @@ def _grads(h, w, y, g, acc_into=None):
     return gh, gw
 
 
-@pytest.mark.parametrize("T,H,V", [(64, 128, 1000), (100, 192, 2053), (257, 256, 4099), (40, 64, 40000)])
+# (40, 64, 140000) walks three 65536-row vocabulary steps, the last one ragged
+@pytest.mark.parametrize("T,H,V", [(64, 128, 1000), (100, 192, 2053), (257, 256, 4099), (40, 64, 40000),
+                                   (40, 64, 140000)])
 def test_backward_parity(T, H, V):
     print(f"[case] bwd T={T} H={H} V={V}", flush=True)
     h, w, y, g = _case(T, H, V, seed=T)
