@@ -13,8 +13,8 @@
 //    "batch-invariant actor forward and sampler log-prob formula", review on the temperature
 //    order: fp32 logits divided by the fp32 temperature inside the chunk).
 // K2 fwd_finalize: folds each row's records in a fixed order (64 fixed segments of consecutive
-//    chunks, each folded in ascending order, then the segments in ascending order — a function
-//    of V only) and writes logprob = (z_y - M) - log S, entropy = log S - U/S, lse = M + log S,
+//    chunks, each folded in ascending order, then the 64 segment states merged in a fixed binary
+//    tree — a function of V only) and writes logprob = (z_y - M) - log S, entropy = log S - U/S, lse = M + log S,
 //    with log S = log N + log1p(B/N), and sum_p2 = Q / S^2.  (verl PR #8026, first review: fp32
 //    log_softmax over the full vocabulary then gather, with entropy and sum_pi_squared of the same
 //    softmax; SkyRL PR #1765, precision-policy commit: logprob 0 for an out-of-vocabulary label.)
@@ -359,20 +359,42 @@ __device__ __forceinline__ Rec fold(Rec s, Rec r) {
   return s;
 }
 
+// Outputs of row t from its folded state: log S = log N + log1p(B / N) keeps tiny entropies
+// relatively exact; the log-prob is (z_y - M) - log S, 0 for a label outside the vocabulary.
+template <bool P2>
+__device__ __forceinline__ void finalize_row(const FwdArgs& a, int t, const Rec& st) {
+  const float logS = logf(st.n) + log1pf(st.b / st.n);
+  const int y = a.labels[t];
+  const bool in_vocab = y >= 0 && y < a.vocab_total;
+  a.logprob[t] = in_vocab ? (a.zy[t] - st.m) - logS : 0.f;
+  if (a.entropy) a.entropy[t] = logS - st.u / (st.n + st.b);
+  if (a.lse) a.lse[t] = st.m + logS;
+  if (P2) {
+    const float S = st.n + st.b;
+    a.sum_p2[t] = st.q / (S * S);
+  }
+}
+
 constexpr int FIN_WAVES = 16; // wavefronts per workgroup
 constexpr int FIN_NSEG = 64;  // fixed number of fold segments per row
 
-// One workgroup folds the rows of TPW tokens (TPW = 16, 32 or 64).  Lane l of a wavefront serves
+// One workgroup folds the rows of TPW tokens (TPW = 16 or 32).  Lane l of a wavefront serves
 // token l % TPW and segment slot l / TPW, so a wavefront covers 64 / TPW segments of each of its
 // tokens per pass and the 16 wavefronts cover all 64 segments in 4 TPW / 64 passes.  Small T takes
 // small TPW, so that lanes are not left idle on missing tokens; large T takes TPW = 32, which gives
-// a workgroup per CU at T = 8192.  How segments are spread over lanes does not change any value:
-// each segment is folded in ascending chunk order, then the 64 segment states in ascending order.
+// a workgroup per CU at T = 8192.  Each segment is folded in ascending chunk order, its records
+// loaded in batches (one batch covers a segment of up to 20 chunks when TPW = 16, i.e. V up to
+// 163840); then the 64 segment states of a token are merged in a fixed binary tree inside one
+// wavefront (lane s holds segment s; at level d = 1, 2, 4, ..., 32 lane s with s % 2d == 0 merges
+// the state of lane s + d into its own), six dependent merges instead of a chain of 64.  Neither
+// the spread of segments over lanes nor the batching changes any value; the order is a function
+// of V only.
 template <bool P2, int TPW>
 __global__ __launch_bounds__(64 * FIN_WAVES) void fwd_finalize_kernel(FwdArgs a, int n_c) {
+  static_assert(FIN_NSEG == 64, "one segment state per lane in the tree");
   constexpr int LPT = 64 / TPW;                      // segment slots per wavefront and pass
   constexpr int PASSES = FIN_NSEG / (FIN_WAVES * LPT);
-  constexpr int BATCH = 16 / PASSES;                 // records per segment loaded before folding
+  constexpr int BATCH = 20 / PASSES;                 // records per segment loaded before folding
   __shared__ Rec part[FIN_NSEG][TPW];
   const int T = a.T;
   const int lane = threadIdx.x & 63;
@@ -414,20 +436,23 @@ __global__ __launch_bounds__(64 * FIN_WAVES) void fwd_finalize_kernel(FwdArgs a,
 #pragma unroll
   for (int j = 0; j < PASSES; ++j) part[sg[j]][tl] = seg[j];
   __syncthreads();
-  if (w != 0 || lane >= TPW || t >= T) return;
-  Rec st = {-__builtin_inff(), 0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-  for (int s = 0; s < FIN_NSEG; ++s) st = fold<P2>(st, part[s][tl]);
-
-  const float logS = logf(st.n) + log1pf(st.b / st.n);
-  const int y = a.labels[t];
-  const bool in_vocab = y >= 0 && y < a.vocab_total;
-  a.logprob[t] = in_vocab ? (a.zy[t] - st.m) - logS : 0.f;
-  if (a.entropy) a.entropy[t] = logS - st.u / (st.n + st.b);
-  if (a.lse) a.lse[t] = st.m + logS;
-  if (P2) {
-    const float S = st.n + st.b;
-    a.sum_p2[t] = st.q / (S * S);
+  // wavefront w merges the segment states of tokens w, w + 16, ... of the workgroup
+  for (int k = w; k < TPW; k += FIN_WAVES) {
+    const int tt = blockIdx.x * TPW + k;
+    if (tt >= T) break;  // k is the same in every lane
+    Rec st = part[lane][k];
+#pragma unroll
+    for (int d = 1; d < FIN_NSEG; d *= 2) {
+      Rec o;
+      o.m = __shfl_down(st.m, d);
+      o.n = __shfl_down(st.n, d);
+      o.b = __shfl_down(st.b, d);
+      o.u = __shfl_down(st.u, d);
+      o.q = P2 ? __shfl_down(st.q, d) : 0.f;
+      const Rec f = fold<P2>(st, o);
+      if ((lane & (2 * d - 1)) == 0) st = f;
+    }
+    if (lane == 0) finalize_row<P2>(a, tt, st);
   }
 }
 
