@@ -40,7 +40,8 @@
  *    returned and nothing is launched.  T == 0 returns LMH_OK and launches nothing.
  *  - Layouts: hidden bf16 [T,H] row-major contiguous; weight bf16 [V,H] row-major contiguous;
  *    labels int32 [T]; all per-row outputs fp32 [T]; gradients fp32 row-major contiguous.
- *  - Requirements: H % 8 == 0, 8 <= H <= 1048576, 1 <= V < 2^31, 0 <= T < 2^31; hidden and
+ *  - Requirements: H % 8 == 0, 8 <= H <= 1048576, 1 <= V < 2^31, 0 <= T < 2^31 and
+ *    T * ceil(V / 128) <= 2^36 (the forward's records; LMH_ERR_UNSUPPORTED otherwise); hidden and
  *    weight 16-byte aligned; labels, per-row arrays and gradients 4-byte aligned; workspace
  *    256-byte aligned.  Non-finite inputs give undefined outputs (no error).
  *  - No C++ exception crosses the ABI.  There is no silent fallback: an unsupported request is

@@ -23,9 +23,11 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 lmh_status_t check_sizes(int64_t T, int64_t H, int64_t V) {
   if (T < 0 || H <= 0 || V <= 0) return LMH_ERR_INVALID_ARG;
   if (H % 8 != 0 || H > MAX_H || V >= MAX_V || T >= MAX_T) return LMH_ERR_UNSUPPORTED;
-  // every size derived below (records, workspace offsets) must fit in 64 bits comfortably
+  // At most 2^36 (row, chunk) records (1.1 TB of workspace, beyond any one device's memory), so
+  // every derived size fits its type: the large-T tile count (about records / 512 < 2^28) is
+  // a 32-bit int in the kernels, record offsets are 64-bit.
   const int64_t n_c = (V + lmh::VOCAB_CHUNK - 1) / lmh::VOCAB_CHUNK;
-  if (T > 0 && n_c > (int64_t(1) << 40) / T) return LMH_ERR_UNSUPPORTED;
+  if (T > 0 && n_c > (int64_t(1) << 36) / T) return LMH_ERR_UNSUPPORTED;
   return LMH_OK;
 }
 

@@ -58,6 +58,9 @@ def test_workspace_sizes(lib):
     assert lmh.lmhead_logprob_fwd_workspace_size(4, 12, 10) == 0     # H % 8 != 0
     assert lmh.lmhead_logprob_fwd_workspace_size(-1, 8, 10) == 0
     assert lmh.lmhead_logprob_fwd_workspace_size(4, 8, 0) == 0
+    # at most 2^36 (row, 128-column chunk) records: 1188 chunks x 2^26 rows is past it
+    assert lmh.lmhead_logprob_fwd_workspace_size(1 << 26, 8, V) == 0
+    assert lmh.lmhead_logprob_fwd_workspace_size(1 << 25, 8, V) > 0
     bwd = lmh.lmhead_logprob_bwd_workspace_size(4096, 5120, V)
     assert bwd >= 4096 * 16384 * 2 * 2 + 5120 * 16384 * 2 + 5120 * 4096 * 2
     # the workspace grows linearly in T for the forward
@@ -79,6 +82,7 @@ def test_fwd_validation_codes(lib):
     assert _fwd(lib, H=0) == lmh.LMH_ERR_INVALID_ARG
     assert _fwd(lib, V=2**31 - 1) == lmh.LMH_ERR_UNSUPPORTED
     assert _fwd(lib, H=8 * (1 << 20)) == lmh.LMH_ERR_UNSUPPORTED
+    assert _fwd(lib, T=1 << 26, V=152064) == lmh.LMH_ERR_UNSUPPORTED  # more than 2^36 records
     assert _fwd(lib, hidden=24) == lmh.LMH_ERR_UNSUPPORTED          # not 16-byte aligned
     assert _fwd(lib, labels=18) == lmh.LMH_ERR_UNSUPPORTED
     assert _fwd(lib, entropy=2) == lmh.LMH_ERR_UNSUPPORTED
