@@ -24,7 +24,7 @@
 // and the MFMA chain are fixed).
 // large-T tile: 256 x 256, 8 wavefronts, ping-pong main loop; XCD tile grouping
 #ifndef LMH_GROUP_M
-#define LMH_GROUP_M 8
+#define LMH_GROUP_M 4
 #endif
 // small-T tiles (T <= 32 and 32 < T <= 64): wavefront grid (WM, WN, NSUB), stages and K step of
 // the spread main loop
@@ -67,6 +67,7 @@ namespace lmh {
 // below every real logit, so it never reaches the max, and exp2 of its shift underflows to 0, so
 // it adds exactly zero to every sum (0 * d is -0 for finite d).
 constexpr float MASKED_LOGIT = -1.0e30f;
+constexpr float LN2 = 0.6931471805599453f;  // converts the shift sum from log2 units
 
 // Options of the record epilogue, fixed per kernel instantiation.
 template <bool SCALED_, bool P2_>
@@ -119,18 +120,26 @@ __device__ __forceinline__ void fwd_records(f32x4 (&acc)[MSUB][NSUB], int lane, 
     // pass 2: count at the max, sum of exp below it, sum of exp * shift (fixed order: m, then i)
     int cnt = 0;
     float b = 0.f, u = 0.f, q = 0.f;
+    // The exponent is formed as z log2(e) - m log2(e) with one fused multiply-add, and the shift is
+    // summed in the same log2 units and converted once per chunk; entries equal to the max are
+    // taken out of b, u (and counted in n) by the comparison z == m itself, so their rounding
+    // residual in the fused shift never reaches the sums.
+    const float mxl = mx * LOG2E;
 #pragma unroll
     for (int m = 0; m < MSUB; ++m)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float d = acc[m][n][i] - mx;
-        const float e = __builtin_amdgcn_exp2f(d * LOG2E);
-        const bool at_max = d == 0.f;
+        const float z = acc[m][n][i];
+        const float d2 = __builtin_fmaf(z, LOG2E, -mxl);
+        const bool at_max = z == mx;
+        const float e = at_max ? 0.f : __builtin_amdgcn_exp2f(d2);
         cnt += at_max;
-        b += at_max ? 0.f : e;
-        u = __builtin_fmaf(e, d, u);
-        if (Opt::P2) q = __builtin_fmaf(e, e, q);
+        b += e;
+        u = __builtin_fmaf(e, d2, u);
+        if (Opt::P2) q = at_max ? q + 1.f : __builtin_fmaf(e, e, q);
       }
+    u = u * LN2;
+
     // the four lanes' partial sums as (s0 + s1) + (s2 + s3): by commutativity of each addition,
     // every lane of the token ends with the same bits
     cnt += __shfl_xor(cnt, 16);
