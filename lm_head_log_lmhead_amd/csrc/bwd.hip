@@ -38,6 +38,68 @@ __device__ __forceinline__ void st_dz(__bf16* p, u32x4 v) {
 constexpr int DZ_PITCH = WAVE_M * 2 + 16;  // bytes per staged token row (padded against conflicts)
 constexpr int BWD_SCHED_WORDS = 16;        // tile counters per vocabulary step (one per XCD)
 
+// dz of a wavefront's tile part: the lane's four consecutive entries 16 m + 4 g4 + (0..3) of token
+// n * 16 + j, rounded to bf16 and staged token-major in LDS at wl.  dz = g (onehot - p) is formed as
+// fmaf(-g, p, label ? g : 0); without an entropy gradient the exponent is one fmaf,
+// z log2(e) - lse log2(e).  The label test compares the label's offset from the lane's entry 0
+// with the entry's constant offset 16 m + i (a label outside the call's rows gives a negative
+// offset).  Unless FULL, entries past the call's rows and tokens past T are zeros.
+template <class Cfg, bool SCALED, bool EGRAD, bool FULL>
+__device__ __forceinline__ void dz_stage(const f32x4 (&acc)[MSUB][Cfg::NSUB], const float* __restrict__ grad,
+                                         const float* __restrict__ lse, const int* __restrict__ labels,
+                                         const float* __restrict__ grad_entropy, const float* __restrict__ entropy,
+                                         float temperature, int T, int V, int vocab_start, int vs0, int wv, int tok0,
+                                         char* wl) {
+  const int lane = threadIdx.x & 63;
+  const int j = acc_col(lane);
+  const int g4 = lane >> 4;
+#pragma unroll
+  for (int n = 0; n < Cfg::NSUB; ++n) {
+    const int tok = tok0 + n * MFMA_MN + j;
+    const bool tok_ok = FULL || tok < T;
+    float g = tok_ok ? grad[tok] : 0.f;
+    const float L = tok_ok ? lse[tok] : 0.f;
+    // the label as a weight row of this call (-1 when another shard's or out of range)
+    const int yg = tok_ok ? labels[tok] : -1;
+    const int y = yg >= vocab_start && yg - vocab_start < V ? yg - vocab_start : -1;
+    const int yl = y - (vs0 + wv + 4 * g4);  // label offset from the lane's entry 0
+    float ge = 0.f, He = 0.f;
+    if (EGRAD) {
+      ge = tok_ok ? grad_entropy[tok] : 0.f;
+      He = tok_ok ? entropy[tok] : 0.f;
+    }
+    if (SCALED) {  // the 1/tau of the chain rule, folded into the per-token factors
+      g = g / temperature;
+      ge = ge / temperature;
+    }
+    const float lL = L * LOG2E;
+#pragma unroll
+    for (int m = 0; m < MSUB; ++m) {
+      f32x4 dv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float z = SCALED ? acc[m][n][i] / temperature : acc[m][n][i];
+        float p, lp = 0.f;
+        if (EGRAD) {
+          lp = z - L;
+          p = __builtin_amdgcn_exp2f(lp * LOG2E);
+        } else {
+          p = __builtin_amdgcn_exp2f(__builtin_fmaf(z, LOG2E, -lL));
+        }
+        float d = __builtin_fmaf(-g, p, yl == m * MFMA_MN + i ? g : 0.f);
+        if (EGRAD) d = d - ge * (p * (lp + He));
+        if (!FULL) {
+          const int v = vs0 + wv + m * MFMA_MN + acc_row(i, lane);
+          d = v < V && tok_ok ? d : 0.f;
+        }
+        dv[i] = d;
+      }
+      *reinterpret_cast<bf16x4*>(wl + (n * MFMA_MN + j) * DZ_PITCH + (m * MFMA_MN + 4 * g4) * 2) =
+          __builtin_convertvector(dv, bf16x4);
+    }
+  }
+}
+
 // With a temperature tau the logits are z / tau and the logit gradient carries 1/tau; with an
 // entropy gradient gE the term -gE p (log p + H) is added (log p = z / tau - lse), as in the
 // forward definition (verl PR #8026 review on the temperature order; the entropy gradient that
@@ -67,49 +129,20 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void bwd_dz_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave % Cfg::WM, wn = wave / Cfg::WM;
-  const int j = acc_col(lane);
   const int g4 = lane >> 4;
   const int wv = v0 + wm * WAVE_M;             // local column of this wavefront's first entry
   const int tok0 = t0 + wn * Cfg::WAVE_N;
   char* wl = lds + wave * Cfg::WAVE_N * DZ_PITCH;
 
-  // dz of the lane's four consecutive entries 16 m + 4 g4 + (0..3) of token n * 16 + j, staged
-  // token-major in LDS
-#pragma unroll
-  for (int n = 0; n < Cfg::NSUB; ++n) {
-    const int tok = tok0 + n * MFMA_MN + j;
-    const bool tok_ok = tok < T;
-    float g = tok_ok ? grad[tok] : 0.f;
-    const float L = tok_ok ? lse[tok] : 0.f;
-    // the label as a weight row of this call (-1 when another shard's or out of range)
-    const int yg = tok_ok ? labels[tok] : -1;
-    const int y = yg >= vocab_start && yg - vocab_start < V ? yg - vocab_start : -1;
-    float ge = 0.f, He = 0.f;
-    if (EGRAD) {
-      ge = tok_ok ? grad_entropy[tok] : 0.f;
-      He = tok_ok ? entropy[tok] : 0.f;
-    }
-    if (SCALED) {  // the 1/tau of the chain rule, folded into the per-token factors
-      g = g / temperature;
-      ge = ge / temperature;
-    }
-#pragma unroll
-    for (int m = 0; m < MSUB; ++m) {
-      bf16x4 pk;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int v = vs0 + wv + m * MFMA_MN + acc_row(i, lane);
-        const float z = SCALED ? acc[m][n][i] / temperature : acc[m][n][i];
-        const float lp = z - L;
-        const float p = __builtin_amdgcn_exp2f(lp * LOG2E);
-        const float oh = v == y ? 1.f : 0.f;
-        float d = g * (oh - p);
-        if (EGRAD) d = d - ge * (p * (lp + He));
-        pk[i] = (__bf16)(v < V && tok_ok ? d : 0.f);
-      }
-      *reinterpret_cast<bf16x4*>(wl + (n * MFMA_MN + j) * DZ_PITCH + (m * MFMA_MN + 4 * g4) * 2) = pk;
-    }
-  }
+  // dz of the lane's entries, staged token-major in LDS (see dz_stage); a wavefront whose 128
+  // rows and WAVE_N tokens all exist (every one but the tail tiles') skips the range tests
+  const bool full = __builtin_amdgcn_readfirstlane(vs0 + wv + WAVE_M <= V && tok0 + Cfg::WAVE_N <= T);
+  if (full)
+    dz_stage<Cfg, SCALED, EGRAD, true>(acc, grad, lse, labels, grad_entropy, entropy, temperature, T, V, vocab_start,
+                                       vs0, wv, tok0, wl);
+  else
+    dz_stage<Cfg, SCALED, EGRAD, false>(acc, grad, lse, labels, grad_entropy, entropy, temperature, T, V,
+                                        vocab_start, vs0, wv, tok0, wl);
   __syncthreads();
   // copy the wavefront's [WAVE_N tokens x 128 entries] block out, 16 bytes per lane
   constexpr int CHUNKS = Cfg::WAVE_N * (WAVE_M / 8);
