@@ -1,5 +1,6 @@
 """GPU parity at the edges of the supported range: the largest hidden size (H = 2^20, a K loop of
-16384 steps) and temperatures far from 1, against the fp64 oracle."""
+16384 steps), the largest token count of the backward (T = 2^22 - 1) and temperatures far from 1,
+against the fp64 oracle."""
 import numpy as np
 import pytest
 import torch
@@ -55,5 +56,36 @@ def test_temperatures_far_from_one(tau):
     np.testing.assert_allclose(_np(p2), ref["sum_p2"], rtol=SUM_P2_RTOL, atol=0)
     rgh, rgw = fp64.backward(x.hidden, x.weight, x.labels, x.grad, temperature=tau, grad_entropy=ge)
     e1, e2 = rel_fro(_np(gh), rgh), rel_fro(_np(gw), rgw)
+    print(f"rel fro grad_hidden {e1:.3e} grad_weight {e2:.3e}", flush=True)
+    assert e1 <= GRAD_REL_FRO and e2 <= GRAD_REL_FRO
+
+
+def test_maximum_token_count():
+    # T = 2^22 - 1, the largest the backward accepts: 16384 persistent forward tiles, a fold grid of
+    # 131072 workgroups, dz^T rows of 2^22 tokens (a 256-row tile spans exactly 2^31 bytes) and a
+    # grad_weight chain of 65536 K steps.  Forward and grad_hidden on sampled rows, grad_weight in
+    # full, and a row split that must give the same bits.
+    T, H, V = (1 << 22) - 1, 8, 130
+    print(f"[case] T={T} H={H} V={V}", flush=True)
+    x = synth.make_inputs(T, H, V, seed=54, weight_std=0.5, with_grad=True)
+    h, w, y, g = to_dev(x.hidden, x.weight, x.labels, x.grad)
+    lp, ent, lse = lmh.forward(h, w, y, entropy=True, want_lse=True)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.random.default_rng(54).integers(0, T, 4000), [0, T - 1]]))
+    ref = fp64.forward_rows(x.hidden, x.weight, x.labels, rows)
+    assert_logprob(_np(lp)[rows], ref["logprob"], "T = 2^22 - 1")
+    assert_entropy(_np(ent)[rows], ref["entropy"], "T = 2^22 - 1")
+    s = 3 * T // 7
+    parts = [lmh.forward(h[a:b], w, y[a:b], entropy=True, want_lse=True) for a, b in ((0, s), (s, T))]
+    torch.cuda.synchronize()
+    for k, full in enumerate((lp, ent, lse)):
+        joined = torch.cat([p[k] for p in parts])
+        assert torch.equal(joined.view(torch.int32), full.view(torch.int32)), f"output {k} changes with the split"
+    del parts
+    gh, gw = lmh.backward(h, w, y, g, lse)
+    torch.cuda.synchronize()
+    rgh = fp64.grad_hidden_rows(x.hidden, x.weight, x.labels, x.grad, rows)
+    rgw = fp64.grad_weight_rows(x.hidden, x.weight, x.labels, x.grad, np.arange(V), row_block=1 << 16)
+    e1, e2 = rel_fro(_np(gh)[rows], rgh), rel_fro(_np(gw), rgw)
     print(f"rel fro grad_hidden {e1:.3e} grad_weight {e2:.3e}", flush=True)
     assert e1 <= GRAD_REL_FRO and e2 <= GRAD_REL_FRO
