@@ -1,6 +1,6 @@
 """GPU parity at the edges of the supported range: the largest hidden size (H = 2^20, a K loop of
-16384 steps), the largest token count of the backward (T = 2^22 - 1) and temperatures far from 1,
-against the fp64 oracle."""
+16384 steps), the largest token count of the backward (T = 2^22 - 1), a vocabulary of 2^24 + 77
+and temperatures far from 1, against the fp64 oracle."""
 import numpy as np
 import pytest
 import torch
@@ -88,4 +88,32 @@ def test_maximum_token_count():
     rgw = fp64.grad_weight_rows(x.hidden, x.weight, x.labels, x.grad, np.arange(V), row_block=1 << 16)
     e1, e2 = rel_fro(_np(gh)[rows], rgh), rel_fro(_np(gw), rgw)
     print(f"rel fro grad_hidden {e1:.3e} grad_weight {e2:.3e}", flush=True)
+    assert e1 <= GRAD_REL_FRO and e2 <= GRAD_REL_FRO
+
+
+def test_large_vocabulary():
+    # V = 2^24 + 77: 131073 record chunks per row (fold segments of ~2048 chunks), 131074 large-T
+    # tiles at T = 300, and 257 vocabulary steps in the backward.  The oracle sees sampled rows in
+    # small blocks (a row of fp64 logits is 134 MB).
+    H, V = 8, (1 << 24) + 77
+    T = 300
+    print(f"[case] T={T} H={H} V={V}", flush=True)
+    x = synth.make_inputs(T, H, V, seed=55, weight_std=0.5, with_grad=True)
+    h, w, y, g = to_dev(x.hidden, x.weight, x.labels, x.grad)
+    lp, ent, lse = lmh.forward(h, w, y, entropy=True, want_lse=True)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.random.default_rng(55).integers(0, T, 24), [0, T - 1]]))
+    ref = fp64.forward_rows(x.hidden, x.weight, x.labels, rows, row_block=4)
+    assert_logprob(_np(lp)[rows], ref["logprob"], "V = 2^24 + 77")
+    assert_entropy(_np(ent)[rows], ref["entropy"], "V = 2^24 + 77")
+    np.testing.assert_allclose(_np(lse)[rows], ref["lse"], rtol=0, atol=2e-3 + 1e-6 * np.abs(ref["lse"]).max())
+    # backward on three rows: all of grad_hidden, sampled grad_weight rows (including the labels')
+    t3 = slice(0, 3)
+    gh, gw = lmh.backward(h[t3], w, y[t3], g[t3], lse[t3])
+    torch.cuda.synchronize()
+    vr = np.unique(np.concatenate([np.random.default_rng(56).integers(0, V, 2000), x.labels[:3].numpy(), [V - 1]]))
+    rgh = fp64.grad_hidden_rows(x.hidden[t3], x.weight, x.labels[t3], x.grad[t3], np.arange(3), row_block=1)
+    rgw = fp64.grad_weight_rows(x.hidden[t3], x.weight, x.labels[t3], x.grad[t3], vr, row_block=1)
+    e1, e2 = rel_fro(_np(gh), rgh), rel_fro(_np(gw)[vr], rgw)
+    print(f"rel fro grad_hidden {e1:.3e} grad_weight (sampled rows) {e2:.3e}", flush=True)
     assert e1 <= GRAD_REL_FRO and e2 <= GRAD_REL_FRO
