@@ -263,7 +263,9 @@ def backward(hidden, weight, labels, grad_logprob, lse, need_hidden=True, need_w
     T, H, V = _dims(hidden, weight)
     dev = hidden.device
     gh = torch.empty((T, H), dtype=torch.float32, device=dev) if need_hidden else None
-    gw = torch.empty((V, H), dtype=torch.float32, device=dev) if need_weight else None
+    # an empty batch contributes nothing: the library leaves the buffers untouched for T == 0
+    alloc = torch.zeros if T == 0 else torch.empty
+    gw = alloc((V, H), dtype=torch.float32, device=dev) if need_weight else None
     ws = _workspace(lmhead_logprob_bwd_workspace_size(T, H, V), dev)
     if temperature == 1.0 and grad_entropy is None and vocab_start == 0:
         lmhead_logprob_bwd(hidden, weight, labels, grad_logprob, lse, gh, gw, False, ws, stream)

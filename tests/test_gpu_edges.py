@@ -117,3 +117,20 @@ def test_large_vocabulary():
     e1, e2 = rel_fro(_np(gh), rgh), rel_fro(_np(gw)[vr], rgw)
     print(f"rel fro grad_hidden {e1:.3e} grad_weight (sampled rows) {e2:.3e}", flush=True)
     assert e1 <= GRAD_REL_FRO and e2 <= GRAD_REL_FRO
+
+
+def test_empty_batch_through_autograd():
+    # T = 0: empty outputs, an empty grad_hidden and a zero grad_weight (the library launches
+    # nothing and leaves gradient buffers untouched, so the binding hands out zeros)
+    H, V = 64, 300
+    print(f"[case] T=0 H={H} V={V}", flush=True)
+    x = synth.make_inputs(1, H, V, seed=57, weight_std=0.05)
+    h = x.hidden.to(dev())[:0].float().requires_grad_(True)
+    w = x.weight.to(dev()).requires_grad_(True)
+    y = x.labels.to(dev())[:0]
+    lp, ent = lmh.logprob(h, w, y, entropy=True)
+    assert lp.shape == (0,) and ent.shape == (0,)
+    (lp.sum() + ent.sum()).backward()
+    torch.cuda.synchronize()
+    assert h.grad.shape == (0, H)
+    assert torch.count_nonzero(w.grad).item() == 0
