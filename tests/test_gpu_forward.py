@@ -9,9 +9,10 @@ import numpy as np
 import pytest
 import torch
 
+import lm_head_log_lmhead_amd as lmh
 import synth
 from oracle import fp64
-from tests.gpu_util import assert_entropy, assert_logprob, fwd, to_dev
+from tests.gpu_util import GRAD_REL_FRO, assert_entropy, assert_logprob, fwd, rel_fro, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -57,12 +58,25 @@ def test_out_of_range_labels():
     assert lp[0] == 0.0 and lp[5] == 0.0 and lp[9] == 0.0 and lp[33] == 0.0 and lp[69] == 0.0
 
 
-def test_vocab_of_one_and_two():
-    h, w, _ = _case(40, 64, 1, seed=5, wstd=0.3)
-    lp, ent, _, _ = _check(h, w, torch.zeros(40, dtype=torch.int32), "V=1")
+@pytest.mark.parametrize("T", [17, 40, 100, 300])   # each token-tile family
+def test_vocab_of_one_and_two(T):
+    h, w, _ = _case(T, 64, 1, seed=5, wstd=0.3)
+    y1 = torch.zeros(T, dtype=torch.int32)
+    y1[T // 2] = -100                                   # out of range: logprob 0, dz = -g p = -g
+    lp, ent, _, _ = _check(h, w, y1, "V=1")
     assert np.all(lp == 0.0) and np.all(ent == 0.0)
-    h, w, y = _case(40, 64, 2, seed=6, wstd=0.3)
-    _check(h, w, y, "V=2")
+    h2, w2, y2 = _case(T, 64, 2, seed=6, wstd=0.3)
+    _check(h2, w2, y2, "V=2")
+    # backward: V = 1 leaves only the out-of-range row's -g p term
+    for hh, ww, yy in ((h, w, y1), (h2, w2, y2)):
+        g = synth.upstream_grad(T, 7)
+        hd, wd, yd, gd = to_dev(hh, ww, yy, g)
+        _, _, lse = lmh.forward(hd, wd, yd, entropy=True, want_lse=True)
+        gh, gw = lmh.backward(hd, wd, yd, gd, lse)
+        torch.cuda.synchronize()
+        rgh, rgw = fp64.backward(hh, ww, yy, g)
+        assert rel_fro(gh.cpu().double().numpy(), rgh) <= GRAD_REL_FRO
+        assert rel_fro(gw.cpu().double().numpy(), rgw) <= GRAD_REL_FRO
 
 
 def test_uniform_logits():
