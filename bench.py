@@ -10,6 +10,11 @@ W warm-up steps, then K timed steps bracketed by torch.cuda.synchronize(); every
 also bracketed by HIP events on the stream the library launches on, which gives the dominant
 kernel's average duration for the roofline.
 
+``ms_per_step`` is the wall-clock mean over the K steps; ``ms_per_step_median`` the median of the
+per-step durations from the events.  The CPU-baseline leg times the fp64 oracle on the first rows
+of the same inputs, and ``parity`` compares the timed run's own outputs with the oracle's on those
+rows (max |d logprob|, max relative entropy error, rows outside the gates).
+
 Prints ONE JSON line.  ``--gpus N`` with N > 1 is not supported: this build runs on one GPU.
 """
 from __future__ import annotations
@@ -53,10 +58,13 @@ def parse():
 
 
 def kernel_sources_digest() -> str:
+    """Digest of every source the library is built from (kernels, host code, the ABI header)."""
     h = hashlib.sha256()
-    for f in ("tile_gemm.hpp", "fwd.hip", "kernels.hpp"):
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+    paths = [os.path.join(CSRC, f) for f in sorted(os.listdir(CSRC))] + [os.path.join(ROOT, "include",
+                                                                                      "lmhead_logprob.h")]
+    for path in paths:
+        with open(path, "rb") as fh:
+            h.update(os.path.basename(path).encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
 
 
@@ -78,10 +86,30 @@ CPU_TARGET_S = 15.0     # seconds of oracle work the automatic CPU sample aims a
 CPU_PROBE_ROWS = 128    # rows timed first to size the automatic sample
 
 
+LOGPROB_ATOL = 2e-3     # |logprob - oracle|
+ENTROPY_RTOL = 1e-3     # |entropy - oracle| <= 1e-3 |oracle| + 1e-7
+ENTROPY_ATOL = 1e-7
+
+
+def parity(ref, lp, ent):
+    """Errors of the timed run's outputs on the oracle's rows: max |d logprob|, max relative
+    entropy error, and the number of rows outside either gate."""
+    n = ref["logprob"].shape[0]
+    d_lp = np.abs(lp[:n] - ref["logprob"])
+    bad = d_lp > LOGPROB_ATOL
+    out = {"rows": int(n), "max_abs_err_logprob": float(d_lp.max())}
+    if ent is not None and "entropy" in ref:
+        d_h = np.abs(ent[:n] - ref["entropy"])
+        out["max_rel_err_entropy"] = float((d_h / np.maximum(np.abs(ref["entropy"]), 1e-300)).max())
+        bad |= d_h > ENTROPY_RTOL * np.abs(ref["entropy"]) + ENTROPY_ATOL
+    out["rows_outside_gates"] = int(bad.sum())
+    return out
+
+
 def cpu_baseline(x, rows: int, name: str, temperature: float = 1.0, sum_p2: bool = False):
     """Times the fp64 CPU oracle (as it stands) on the first `rows` rows of the same inputs; with
     rows < 0 the sample is sized from a short probe to about CPU_TARGET_S seconds (whole multiples
-    of the probe, at most every row)."""
+    of the probe, at most every row).  Returns the baseline and the oracle's outputs."""
     from oracle import fp64
     try:
         from threadpoolctl import threadpool_info
@@ -99,11 +127,11 @@ def cpu_baseline(x, rows: int, name: str, temperature: float = 1.0, sum_p2: bool
     h = x.hidden[:rows]
     y = x.labels[:rows]
     t0 = time.perf_counter()
-    fp64.forward(h, W, y, entropy=True, temperature=temperature, sum_p2=sum_p2)
+    ref = fp64.forward(h, W, y, entropy=True, temperature=temperature, sum_p2=sum_p2)
     dt = time.perf_counter() - t0
     return {"value": rows / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": f"first {rows} of {x.hidden.shape[0]} rows of {name} (fp64 numpy, logprob+entropy), "
-                      f"{dt:.1f} s"}
+                      f"{dt:.1f} s"}, ref
 
 
 def main():
@@ -188,6 +216,7 @@ def main():
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    step_ms = [e[0].elapsed_time(e[-1]) for e in evs]               # ms, each step on the stream
     k1 = sum(e[0].elapsed_time(e[1]) for e in evs) / a.steps       # ms, stage 1 (logit tiles + records)
     k2 = sum(e[1].elapsed_time(e[2]) for e in evs) / a.steps       # ms, stage 2 (fold)
     kb = sum(e[2].elapsed_time(e[3]) for e in evs) / a.steps if wl.backward else 0.0
@@ -215,6 +244,8 @@ def main():
         "steps": a.steps,
         "warmup": a.warmup,
         "ms_per_step": ms,
+        "ms_per_step_median": float(np.median(step_ms)),
+        "ms_per_step_mean_events": float(np.mean(step_ms)),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -237,7 +268,9 @@ def main():
     if a.cpu_sample_rows != 0:
         print(f"[bench] timing the CPU oracle ({'automatic sample' if a.cpu_sample_rows < 0 else a.cpu_sample_rows} "
               "rows)", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(x, min(a.cpu_sample_rows, T), a.workload, tau, wl.sum_p2)
+        out["cpu_baseline"], ref = cpu_baseline(x, min(a.cpu_sample_rows, T), a.workload, tau, wl.sum_p2)
+        # the timed run's own outputs (the last timed step's) against the oracle on the same rows
+        out["parity"] = parity(ref, lp.cpu().double().numpy(), None if ent is None else ent.cpu().double().numpy())
     print(json.dumps(out), flush=True)
 
 

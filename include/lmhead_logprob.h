@@ -40,7 +40,7 @@
  *    returned and nothing is launched.  T == 0 returns LMH_OK and launches nothing.
  *  - Layouts: hidden bf16 [T,H] row-major contiguous; weight bf16 [V,H] row-major contiguous;
  *    labels int32 [T]; all per-row outputs fp32 [T]; gradients fp32 row-major contiguous.
- *  - Requirements: H % 8 == 0, 8 <= H <= 1048576, 1 <= V < 2^31, 0 <= T < 2^31 and
+ *  - Requirements: H % 8 == 0, 8 <= H <= 1048576, 1 <= V < 2^31 - 2^16, 0 <= T < 2^31 - 2^16 and
  *    T * ceil(V / 128) <= 2^36 (the forward's records; LMH_ERR_UNSUPPORTED otherwise); hidden and
  *    weight 16-byte aligned; labels, per-row arrays and gradients 4-byte aligned; workspace
  *    256-byte aligned.  Non-finite inputs give undefined outputs (no error).
@@ -75,7 +75,8 @@ typedef enum {
 
 /* Bytes of workspace lmhead_logprob_fwd needs (also the stage entry points below).  Returns 0 for
  * invalid sizes.  The workspace holds one 20-byte record per (row, 128-column vocabulary chunk),
- * one float per row and 256 bytes of tile-scheduler counters; its initial contents do not matter.
+ * one float per row, 256 bytes of tile-scheduler counters and one int per chunk; its initial
+ * contents do not matter.
  * Calls that may run concurrently need separate workspaces. */
 LMH_API size_t lmhead_logprob_fwd_workspace_size(int64_t T, int64_t H, int64_t V);
 
@@ -157,7 +158,8 @@ LMH_API lmh_status_t lmhead_logprob_fwd_ex(const void* hidden, const void* weigh
  * the owner of a label contributes its logit).  Requirements: vocab_start a multiple of 128;
  * vocab_start + V <= vocab_total (LMH_ERR_INVALID_ARG otherwise); V a multiple of 128 unless the
  * shard ends at vocab_total (LMH_ERR_UNSUPPORTED otherwise).  want_sum_p2 (0 or 1) records what
- * sum_p2 needs; finalize may only be asked for sum_p2 if every shard was run with it. */
+ * sum_p2 needs; finalize asked for sum_p2 after a shard was run without it writes NaN to sum_p2
+ * (the workspace keeps one flag per 128-row chunk saying whether its squared sums were recorded). */
 LMH_API lmh_status_t lmhead_logprob_fwd_partials_ex(const void* hidden, const void* weight, const int32_t* labels,
                                                     int64_t T, int64_t H, int64_t V, float temperature,
                                                     int64_t vocab_start, int64_t vocab_total, int want_sum_p2,
@@ -176,8 +178,8 @@ LMH_API lmh_status_t lmhead_logprob_fwd_finalize_ex(const int32_t* labels, int64
  * of a label contributes it).  grad_weight [V,H] receives the shard's rows, bitwise equal to those
  * rows of a call on the whole weight; grad_hidden [T,H] receives this shard's share, dz[:, rows] .
  * weight, which the caller adds over the shards (tensor-parallel: the all-reduce of grad_hidden).
- * vocab_start = 0 is the whole vocabulary.  vocab_start < 0 or vocab_start + V >= 2^31 gives
- * LMH_ERR_INVALID_ARG. */
+ * vocab_start = 0 is the whole vocabulary.  vocab_start < 0 or vocab_start + V >= 2^31 - 2^16
+ * gives LMH_ERR_INVALID_ARG. */
 LMH_API lmh_status_t lmhead_logprob_bwd_ex(const void* hidden, const void* weight, const int32_t* labels,
                                            int64_t T, int64_t H, int64_t V, float temperature,
                                            int64_t vocab_start, const float* grad_logprob, const float* lse,

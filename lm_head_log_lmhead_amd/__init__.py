@@ -278,9 +278,13 @@ def backward(hidden, weight, labels, grad_logprob, lse, need_hidden=True, need_w
 class _FusedLogprob(torch.autograd.Function):
     @staticmethod
     def forward(ctx, hidden, weight, labels, want_entropy, temperature):
-        lp, ent, lse = forward(hidden, weight, labels, entropy=want_entropy, want_lse=True, temperature=temperature)
-        ctx.save_for_backward(hidden, weight, labels, lse, ent)
+        # hidden arrives in the caller's dtype; the projection takes it in the weight's dtype, and
+        # the gradient goes back in the caller's dtype with no rounding to bf16 on the way
+        h = hidden.to(weight.dtype).contiguous()
+        lp, ent, lse = forward(h, weight, labels, entropy=want_entropy, want_lse=True, temperature=temperature)
+        ctx.save_for_backward(h, weight, labels, lse, ent)
         ctx.temperature = temperature
+        ctx.hidden_dtype = hidden.dtype
         ctx.set_materialize_grads(False)
         return lp, ent
 
@@ -295,6 +299,10 @@ class _FusedLogprob(torch.autograd.Function):
         ge = None if grad_ent is None else grad_ent.contiguous().to(torch.float32)
         gh, gw = backward(hidden, weight, labels, g, lse, ctx.needs_input_grad[0], ctx.needs_input_grad[1],
                           temperature=ctx.temperature, grad_entropy=ge, entropy=ent if ge is not None else None)
+        if gh is not None:
+            gh = gh.to(ctx.hidden_dtype)
+        if gw is not None:
+            gw = gw.to(weight.dtype)
         return gh, gw, None, None, None
 
 
@@ -302,16 +310,21 @@ def logprob(hidden: torch.Tensor, weight: torch.Tensor, labels: torch.Tensor, en
             temperature: float = 1.0):
     """Fused LM-head log-prob with autograd.
 
-    hidden [..., H] (any float dtype; cast to weight's dtype before the projection, and the
-    gradient cast back, as the pages' adapter does), weight [V, H] bf16, labels [...] integer.
-    Leading dimensions are flattened to token rows.  The logits are divided by the fp32
+    hidden [..., H] (any float dtype; cast to weight's dtype before the projection, and the fp32
+    gradient returned in hidden's dtype, as the pages' adapter does), weight [V, H] bf16, labels
+    [...] integer.  Leading dimensions are flattened to token rows.  Labels outside [0, V) of any
+    integer width follow the out-of-range rule (they are mapped to -1 before the int32 conversion,
+    so a wide label never wraps onto a vocabulary id).  The logits are divided by the fp32
     temperature before the softmax.  Returns (logprob [...], entropy [...] or None), fp32; both
     are differentiable (the entropy's gradient is -p (log p + entropy) per logit)."""
     if weight.dtype != torch.bfloat16:
         raise ValueError("weight must be bf16")
+    if labels.dtype.is_floating_point or labels.dtype.is_complex or labels.dtype == torch.bool:
+        raise ValueError(f"labels must be an integer tensor, got {labels.dtype}")
     lead = hidden.shape[:-1]
     h2 = hidden.reshape(-1, hidden.shape[-1])
-    h2 = h2.to(weight.dtype).contiguous()   # differentiable: grad_hidden is cast back by autograd
-    y = labels.reshape(-1).to(torch.int32).contiguous()
+    V = weight.shape[0]
+    y = labels.reshape(-1)
+    y = torch.where((y >= 0) & (y < V), y, torch.full_like(y, -1)).to(torch.int32).contiguous()
     lp, ent = _FusedLogprob.apply(h2, weight.contiguous(), y, entropy, float(temperature))
     return lp.reshape(lead), (ent.reshape(lead) if ent is not None else None)

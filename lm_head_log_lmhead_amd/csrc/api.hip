@@ -11,8 +11,11 @@ namespace {
 using lmh::FwdArgs;
 
 constexpr int64_t MAX_H = 1 << 20;
-constexpr int64_t MAX_V = INT32_MAX;  // exclusive bound 2^31 - 1 rows
-constexpr int64_t MAX_T = INT32_MAX;
+// Exclusive bounds on V (also vocab_start + V of a shard) and T.  The kernels index vocabulary rows
+// and tokens with 32-bit ints, including indices rounded up to a whole tile (256) or a whole
+// backward step (65536 rows), so both stay 2^16 below 2^31.
+constexpr int64_t MAX_V = (int64_t(1) << 31) - (int64_t(1) << 16);
+constexpr int64_t MAX_T = (int64_t(1) << 31) - (int64_t(1) << 16);
 // backward: token-major transposed operands are read through 32-bit buffer offsets (256 rows x T)
 constexpr int64_t MAX_T_BWD = int64_t(1) << 22;
 
@@ -32,11 +35,12 @@ lmh_status_t check_sizes(int64_t T, int64_t H, int64_t V) {
 }
 
 struct FwdWs {
-  size_t rec_off, rec2_off, zy_off, sched_off, total;
+  size_t rec_off, rec2_off, zy_off, sched_off, p2ok_off, total;
 };
 
 // Forward workspace for a vocabulary of V rows: records and squared-sum records for every
-// 128-row chunk, label logits, tile counters.
+// 128-row chunk, label logits, tile counters, and one flag per chunk telling whether its
+// squared-sum records were written.
 FwdWs fwd_ws(int64_t T, int64_t V) {
   const int64_t n_c = (V + lmh::VOCAB_CHUNK - 1) / lmh::VOCAB_CHUNK;
   FwdWs w;
@@ -44,7 +48,8 @@ FwdWs fwd_ws(int64_t T, int64_t V) {
   w.rec2_off = align256((size_t)n_c * (size_t)T * 16);
   w.zy_off = w.rec2_off + align256((size_t)n_c * (size_t)T * 4);
   w.sched_off = w.zy_off + align256((size_t)T * 4);
-  w.total = w.sched_off + align256(lmh::SCHED_WORDS * sizeof(int));
+  w.p2ok_off = w.sched_off + align256(lmh::SCHED_WORDS * sizeof(int));
+  w.total = w.p2ok_off + align256((size_t)n_c * sizeof(int));
   return w;
 }
 
@@ -104,6 +109,7 @@ FwdArgs make_fwd_args(const void* hidden, const void* weight, const int32_t* lab
   a.rec2 = reinterpret_cast<float*>(ws + w.rec2_off);
   a.zy = reinterpret_cast<float*>(ws + w.zy_off);
   a.sched = reinterpret_cast<int*>(ws + w.sched_off);
+  a.p2ok = reinterpret_cast<int*>(ws + w.p2ok_off);
   a.logprob = logprob;
   a.entropy = entropy;
   a.lse = lse;
@@ -195,7 +201,7 @@ lmh_status_t bwd_impl(const void* hidden, const void* weight, const int32_t* lab
   LMH_TRY(check_sizes(T, H, V));
   if (accumulate_grad_weight != 0 && accumulate_grad_weight != 1) return LMH_ERR_INVALID_ARG;
   LMH_TRY(check_temperature(temperature));
-  if (vocab_start < 0 || vocab_start > MAX_V - V) return LMH_ERR_INVALID_ARG;
+  if (vocab_start < 0 || vocab_start + V >= MAX_V) return LMH_ERR_INVALID_ARG;
   if (T >= MAX_T_BWD) return LMH_ERR_UNSUPPORTED;
   if (T == 0) return LMH_OK;  // no rows: nothing is launched and the gradient buffers are untouched
   LMH_TRY(check_inputs(hidden, weight, labels));

@@ -212,6 +212,8 @@ __device__ __forceinline__ void tile_records(f32x4 (&acc)[MSUB][Cfg::NSUB], int 
   if (wave_v0 >= a.V) return;  // this wavefront's chunk lies wholly past the weight rows
   const int tok0 = t0 + wn * Cfg::WAVE_N;
   const int chunk = (a.vocab_start + wave_v0) / WAVE_M;
+  // the chunk's first token tile marks whether its squared-sum records exist
+  if (t0 == 0 && wn == 0 && lane == 0) a.p2ok[chunk] = Opt::P2 ? 1 : 0;
   if (wave_v0 + WAVE_M <= a.V)
     fwd_records<Cfg::NSUB, false, Opt>(acc, lane, wave_v0, tok0, a.V, lw, a, chunk);
   else
@@ -387,7 +389,7 @@ __device__ __forceinline__ void finalize_row(const FwdArgs& a, int t, const Rec&
 constexpr int FIN_WAVES = 16; // wavefronts per workgroup
 constexpr int FIN_NSEG = 64;  // fixed number of fold segments per row
 
-// One workgroup folds the rows of TPW tokens (TPW = 16 or 32).  Lane l of a wavefront serves
+// A workgroup folds a block of TPW tokens at a time (TPW = 16 or 32).  Lane l of a wavefront serves
 // token l % TPW and segment slot l / TPW, so a wavefront covers 64 / TPW segments of each of its
 // tokens per pass and the 16 wavefronts cover all 64 segments in 4 TPW / 64 passes.  Small T takes
 // small TPW, so that lanes are not left idle on missing tokens; large T takes TPW = 32, which gives
@@ -399,17 +401,16 @@ constexpr int FIN_NSEG = 64;  // fixed number of fold segments per row
 // the spread of segments over lanes nor the batching changes any value; the order is a function
 // of V only.
 template <bool P2, int TPW>
-__global__ __launch_bounds__(64 * FIN_WAVES) void fwd_finalize_kernel(FwdArgs a, int n_c) {
+__device__ __forceinline__ void fold_row_block(const FwdArgs& a, int n_c, int blk, Rec (&part)[FIN_NSEG][TPW]) {
   static_assert(FIN_NSEG == 64, "one segment state per lane in the tree");
   constexpr int LPT = 64 / TPW;                      // segment slots per wavefront and pass
   constexpr int PASSES = FIN_NSEG / (FIN_WAVES * LPT);
   constexpr int BATCH = 20 / PASSES;                 // records per segment loaded before folding
-  __shared__ Rec part[FIN_NSEG][TPW];
   const int T = a.T;
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int tl = lane % TPW;
-  const int t = blockIdx.x * TPW + tl;
+  const int t = blk * TPW + tl;
   const bool t_ok = t < T;
   int sg[PASSES], lo[PASSES], len[PASSES];
   Rec seg[PASSES];
@@ -434,7 +435,9 @@ __global__ __launch_bounds__(64 * FIN_WAVES) void fwd_finalize_kernel(FwdArgs a,
         const bool ok = t_ok && c < len[j];
         const size_t at = (size_t)(lo[j] + c) * (size_t)T + t;
         r[j][i] = ok ? a.rec[at] : (f32x4)(0.f);
-        r2[j][i] = (P2 && ok) ? a.rec2[at] : 0.f;
+        // a chunk whose partials ran without squared sums gives NaN, which the fold carries to
+        // the row's sum_p2
+        r2[j][i] = (P2 && ok) ? (a.p2ok[lo[j] + c] ? a.rec2[at] : __builtin_nanf("")) : 0.f;
       }
 #pragma unroll
     for (int j = 0; j < PASSES; ++j)
@@ -447,7 +450,7 @@ __global__ __launch_bounds__(64 * FIN_WAVES) void fwd_finalize_kernel(FwdArgs a,
   __syncthreads();
   // wavefront w merges the segment states of tokens w, w + 16, ... of the workgroup
   for (int k = w; k < TPW; k += FIN_WAVES) {
-    const int tt = blockIdx.x * TPW + k;
+    const int tt = blk * TPW + k;
     if (tt >= T) break;  // k is the same in every lane
     Rec st = part[lane][k];
 #pragma unroll
@@ -462,6 +465,18 @@ __global__ __launch_bounds__(64 * FIN_WAVES) void fwd_finalize_kernel(FwdArgs a,
       if ((lane & (2 * d - 1)) == 0) st = f;
     }
     if (lane == 0) finalize_row<P2>(a, tt, st);
+  }
+}
+
+// Grid-stride over the row blocks, so that the grid stays bounded for any T.
+constexpr int FIN_MAX_GRID = 1 << 16;
+
+template <bool P2, int TPW>
+__global__ __launch_bounds__(64 * FIN_WAVES) void fwd_finalize_kernel(FwdArgs a, int n_c, int nblk) {
+  __shared__ Rec part[FIN_NSEG][TPW];
+  for (int blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
+    fold_row_block<P2, TPW>(a, n_c, blk, part);
+    __syncthreads();  // the next block's segment states overwrite part
   }
 }
 
@@ -541,10 +556,11 @@ void launch_fwd_partials(const FwdArgs& a, hipStream_t stream) {
 template <int TPW>
 static void launch_finalize_tpw(const FwdArgs& a, int n_c, hipStream_t stream) {
   const int nblk = (a.T + TPW - 1) / TPW;
+  const dim3 grid(min(nblk, FIN_MAX_GRID));
   if (a.sum_p2)
-    hipLaunchKernelGGL((fwd_finalize_kernel<true, TPW>), dim3(nblk), dim3(64 * FIN_WAVES), 0, stream, a, n_c);
+    hipLaunchKernelGGL((fwd_finalize_kernel<true, TPW>), grid, dim3(64 * FIN_WAVES), 0, stream, a, n_c, nblk);
   else
-    hipLaunchKernelGGL((fwd_finalize_kernel<false, TPW>), dim3(nblk), dim3(64 * FIN_WAVES), 0, stream, a, n_c);
+    hipLaunchKernelGGL((fwd_finalize_kernel<false, TPW>), grid, dim3(64 * FIN_WAVES), 0, stream, a, n_c, nblk);
 }
 
 void launch_fwd_finalize(const FwdArgs& a, hipStream_t stream) {

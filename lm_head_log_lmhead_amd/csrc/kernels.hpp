@@ -35,6 +35,7 @@ struct FwdArgs {
   float* rec2;        // [n_c][T] sum of exp(2 (z - max)) per chunk
   float* zy;          // [T] label logits (divided by the temperature)
   int* sched;         // [SCHED_WORDS] tile counters, reset by the partials launch
+  int* p2ok;          // [n_c] 1 if the chunk's rec2 was written by the last partials run over it
   float* logprob;
   float* entropy;
   float* lse;

@@ -52,3 +52,37 @@ def rel_fro(got, want):
 
 def bits(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().contiguous().view(torch.int32).numpy()
+
+
+def label_rows(labels, V) -> np.ndarray:
+    """Boolean [V]: vocabulary rows that hold the label of some token (their grad_weight row carries
+    a label term g_t h_t besides the softmax term)."""
+    y = np.asarray(labels, dtype=np.int64)
+    mask = np.zeros(V, dtype=bool)
+    mask[y[(y >= 0) & (y < V)]] = True
+    return mask
+
+
+def assert_softmax_rows(got, want, is_label, what=""):
+    """grad_weight rows that hold no label carry only the softmax term -sum_t g_t p_tv h_t, which is
+    a small share of the whole matrix's norm: they are gated on their own, as a block and row by
+    row, so a wrong p cannot hide behind the label rows."""
+    nl = ~np.asarray(is_label, dtype=bool)
+    assert nl.any(), f"{what}: no non-label row to check"
+    block = rel_fro(got[nl], want[nl])
+    per_row = np.linalg.norm(got[nl] - want[nl], axis=1) / np.maximum(np.linalg.norm(want[nl], axis=1), 1e-300)
+    worst = int(np.argmax(per_row))
+    print(f"{what} non-label rows: {int(nl.sum())}, block rel fro {block:.3e}, worst row rel {per_row[worst]:.3e}",
+          flush=True)
+    assert block <= GRAD_REL_FRO, f"{what} non-label grad_weight rows: rel fro {block:.3e}"
+    assert per_row[worst] <= GRAD_REL_FRO, f"{what} non-label grad_weight row {worst}: rel err {per_row[worst]:.3e}"
+
+
+def column_sum_target(hidden, labels, grad, V) -> np.ndarray:
+    """sum_v grad_weight[v, :] in closed form.  Each row of dz sums to g_t (1[y_t in range] - 1), so
+    the column sums are -sum over out-of-range tokens of g_t h_t (fp64 from the exact inputs)."""
+    h = hidden.detach().cpu().double().numpy()
+    g = grad.detach().cpu().double().numpy()
+    y = labels.detach().cpu().long().numpy()
+    oov = (y < 0) | (y >= V)
+    return -(g[oov, None] * h[oov]).sum(axis=0)

@@ -81,6 +81,11 @@ def test_fwd_validation_codes(lib):
     assert _fwd(lib, H=12) == lmh.LMH_ERR_UNSUPPORTED
     assert _fwd(lib, H=0) == lmh.LMH_ERR_INVALID_ARG
     assert _fwd(lib, V=2**31 - 1) == lmh.LMH_ERR_UNSUPPORTED
+    # the header's bounds: V < 2^31 - 2^16 and T < 2^31 - 2^16 (tile-rounded indices stay in int32)
+    assert lmh.lmhead_logprob_fwd_workspace_size(1, 8, 2**31 - 2**16) == 0
+    assert lmh.lmhead_logprob_fwd_workspace_size(1, 8, 2**31 - 2**16 - 1) > 0
+    assert lmh.lmhead_logprob_fwd_workspace_size(2**31 - 2**16, 8, 128) == 0
+    assert lmh.lmhead_logprob_fwd_workspace_size(2**31 - 2**16 - 1, 8, 128) > 0
     assert _fwd(lib, H=8 * (1 << 20)) == lmh.LMH_ERR_UNSUPPORTED
     assert _fwd(lib, T=1 << 26, V=152064) == lmh.LMH_ERR_UNSUPPORTED  # more than 2^36 records
     assert _fwd(lib, hidden=24) == lmh.LMH_ERR_UNSUPPORTED          # not 16-byte aligned
@@ -164,6 +169,8 @@ def test_extended_entry_validation_codes(lib):
     assert bwd_ex(1.3, wsb=64) == lmh.LMH_ERR_WORKSPACE_TOO_SMALL
     assert bwd_ex(1.3, gh=None, gw=None, ge=16, ent=16) == lmh.LMH_OK
     assert bwd_ex(1.0, vs=-128) == lmh.LMH_ERR_INVALID_ARG           # vocabulary shard before id 0
-    assert bwd_ex(1.0, vs=2**31 - 10) == lmh.LMH_ERR_INVALID_ARG     # shard past the 31-bit id range
-    assert bwd_ex(1.0, vs=2**31 - 11, gh=None, gw=None) == lmh.LMH_OK
+    max_v = 2**31 - 2**16                                            # vocabulary ids stay below this
+    assert bwd_ex(1.0, vs=max_v - 10) == lmh.LMH_ERR_INVALID_ARG     # shard past the id range
+    assert bwd_ex(1.0, vs=max_v - 11, gh=None, gw=None) == lmh.LMH_OK
     assert bwd_ex(1.0, vs=77, gh=None, gw=None) == lmh.LMH_OK        # any start: no records are written
+

@@ -6,7 +6,7 @@ import torch
 import lm_head_log_lmhead_amd as lmh
 import synth
 from oracle import fp64
-from tests.gpu_util import GRAD_REL_FRO, bits, dev, rel_fro, to_dev
+from tests.gpu_util import GRAD_REL_FRO, assert_softmax_rows, bits, dev, label_rows, rel_fro, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -38,6 +38,7 @@ def test_backward_parity(T, H, V):
     e2 = rel_fro(gw.cpu().double().numpy(), rgw)
     print(f"rel fro grad_hidden {e1:.3e} grad_weight {e2:.3e}", flush=True)
     assert e1 <= GRAD_REL_FRO and e2 <= GRAD_REL_FRO
+    assert_softmax_rows(gw.cpu().double().numpy(), rgw, label_rows(y.numpy(), V), f"{T}x{H}x{V}")
 
 
 def test_zero_hidden_gives_zero_grad_weight():

@@ -10,7 +10,8 @@ import torch
 import lm_head_log_lmhead_amd as lmh
 import synth
 from oracle import fp64
-from tests.gpu_util import GRAD_REL_FRO, assert_entropy, assert_logprob, bits, dev, rel_fro
+from tests.gpu_util import (GRAD_REL_FRO, assert_entropy, assert_logprob, assert_softmax_rows, bits, dev,
+                            label_rows, rel_fro)
 
 pytestmark = pytest.mark.gpu
 
@@ -86,6 +87,9 @@ def test_T4096_H5120_V152064_backward_sampled():
     e2 = rel_fro(gw.cpu().double().numpy()[vrows], rgw)
     print(f"grad_weight rel fro on 16 rows {e2:.3e}", flush=True)
     assert e1 <= GRAD_REL_FRO and e2 <= GRAD_REL_FRO
+    # the sampled rows that hold no label carry only the softmax term: gated on their own
+    is_label = label_rows(x.labels.numpy(), x.weight.shape[0])[vrows]
+    assert_softmax_rows(gw.cpu().double().numpy()[vrows], rgw, is_label, name)
 
     # bitwise: grad_hidden rows do not depend on the batch split; grad_weight accumulated over a
     # split at a multiple of 64 tokens reproduces the single call

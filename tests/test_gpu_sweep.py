@@ -4,8 +4,8 @@ Each case draws T (in the small-, mid- and large-tile ranges), H (any multiple o
 640, so K can be shorter than one 64-wide step), V (1 to 4999, ragged against every tile) and
 whether a temperature and sum_p2 are asked for, plants two out-of-range labels, and checks
 through the C ABI, element by element against the fp64 oracle: log-prob, entropy, lse, sum_p2,
-and both gradients.  It also checks that splitting the rows at a drawn point into two calls gives
-the same bits as one call.  Sizes keep the oracle to a fraction of a second per case."""
+and both gradients (grad_weight rows that hold no label also on their own).  It also checks that
+splitting the rows at a drawn point into two calls gives the same bits as one call.  Sizes keep the oracle to a fraction of a second per case."""
 import numpy as np
 import pytest
 import torch
@@ -13,7 +13,8 @@ import torch
 import lm_head_log_lmhead_amd as lmh
 import synth
 from oracle import fp64
-from tests.gpu_util import GRAD_REL_FRO, assert_entropy, assert_logprob, bits, rel_fro, to_dev
+from tests.gpu_util import (GRAD_REL_FRO, assert_entropy, assert_logprob, assert_softmax_rows, bits, label_rows,
+                            rel_fro, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -74,3 +75,6 @@ def test_random_case(i, T, H, V, tau, p2, split):
     rgh, rgw = fp64.backward(x.hidden, x.weight, y, x.grad, temperature=tau)
     assert rel_fro(gh.cpu().double().numpy(), rgh) <= GRAD_REL_FRO, f"sweep {i} grad_hidden"
     assert rel_fro(gw.cpu().double().numpy(), rgw) <= GRAD_REL_FRO, f"sweep {i} grad_weight"
+    is_label = label_rows(y.numpy(), V)
+    if not is_label.all():
+        assert_softmax_rows(gw.cpu().double().numpy(), rgw, is_label, f"sweep {i}")
