@@ -33,7 +33,8 @@
  *
  * Conventions for every entry point:
  *  - Pointers are DEVICE pointers owned by the caller.  The library never allocates, frees or
- *    synchronizes, and holds no mutable global state; it is thread-safe.
+ *    synchronizes, and holds no mutable global state except the allocation-free forward's
+ *    per-device scratch array (see lmhead_logprob_fwd_noalloc); it is thread-safe.
  *  - Work is enqueued on `stream` and the call returns; outputs are valid when the stream reaches
  *    that point.  `stream` may be NULL (the default stream).
  *  - Arguments are validated on the host before anything is launched.  On failure the status is
@@ -186,6 +187,25 @@ LMH_API lmh_status_t lmhead_logprob_bwd_ex(const void* hidden, const void* weigh
                                            const float* grad_entropy, const float* entropy,
                                            float* grad_hidden, float* grad_weight, int accumulate_grad_weight,
                                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---- Allocation-free forward ---------------------------------------------------------------
+ *
+ * For callers that cannot allocate device memory or pass a workspace: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same arguments and results as
+ * lmhead_logprob_fwd (the same kernels, so the same bits) without the workspace: the library
+ * keeps one built-in scratch array of LMH_NOALLOC_SCRATCH_BYTES per device, which each device
+ * holds until the process ends.  The call makes no allocation of any kind.
+ * Limit: lmhead_logprob_fwd_workspace_size(T, H, V) <= LMH_NOALLOC_SCRATCH_BYTES (20 bytes per
+ * row and 128-row vocabulary chunk, about T * ceil(V / 128) <= 3.3e6, e.g. T <= 2823 at
+ * V = 152064); larger calls return LMH_ERR_WORKSPACE_TOO_SMALL with nothing launched.
+ * Every call on a device uses that device's one array: calls that may overlap on one device (on
+ * different streams, or from different host threads without ordering) race and give undefined
+ * results; calls ordered on one stream are safe.  The first call on a device looks up the array's
+ * device address (hipGetSymbolAddress) and keeps it; the device is the current one. */
+#define LMH_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+LMH_API lmh_status_t lmhead_logprob_fwd_noalloc(const void* hidden, const void* weight, const int32_t* labels,
+                                                int64_t T, int64_t H, int64_t V,
+                                                float* logprob, float* entropy, float* lse, hipStream_t stream);
 
 /* Static English text for a status code (never NULL). */
 LMH_API const char* lmhead_status_string(lmh_status_t s);

@@ -42,8 +42,12 @@ _SIGNATURES = {
     "lmhead_logprob_fwd_finalize_ex": (_INT, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _SZ, _P]),
     "lmhead_logprob_bwd_ex": (_INT, [_P, _P, _P, _I64, _I64, _I64, _F, _I64, _P, _P, _P, _P, _P, _P, _INT, _P, _SZ,
                                      _P]),
+    "lmhead_logprob_fwd_noalloc": (_INT, [_P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P]),
     "lmhead_status_string": (ctypes.c_char_p, [_INT]),
 }
+
+# Size of the allocation-free forward's built-in scratch array (LMH_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
 
 _lib = None
 
@@ -167,6 +171,17 @@ def lmhead_logprob_bwd(hidden, weight, labels, grad_logprob, lse, grad_hidden=No
     _check(lib().lmhead_logprob_bwd(_ptr(hidden), _ptr(weight), _ptr(labels), T, H, V, _ptr(grad_logprob), _ptr(lse),
                                     _ptr(grad_hidden), _ptr(grad_weight), int(bool(accumulate_grad_weight)),
                                     _ptr(workspace), ws_bytes, _stream(stream)), "lmhead_logprob_bwd")
+
+
+def lmhead_logprob_fwd_noalloc(hidden, weight, labels, logprob, entropy=None, lse=None, stream=None) -> None:
+    T, H, V = _dims(hidden, weight)
+    _check_tensor(hidden, "hidden", torch.bfloat16)
+    _check_tensor(weight, "weight", torch.bfloat16)
+    _check_tensor(labels, "labels", torch.int32, T)
+    for t, n in ((logprob, "logprob"), (entropy, "entropy"), (lse, "lse")):
+        _check_tensor(t, n, torch.float32, T)
+    _check(lib().lmhead_logprob_fwd_noalloc(_ptr(hidden), _ptr(weight), _ptr(labels), T, H, V, _ptr(logprob),
+                                            _ptr(entropy), _ptr(lse), _stream(stream)), "lmhead_logprob_fwd_noalloc")
 
 
 def _nbytes(workspace) -> int:

@@ -4,7 +4,15 @@
 
 #include <math.h>
 
+#include <atomic>
+
 #include "kernels.hpp"
+
+// Workspace of lmhead_logprob_fwd_noalloc: one array per device, alive until the process ends.
+// In host code `scratch` names a host-side stand-in, not the device memory: the device address is
+// looked up with hipGetSymbolAddress (scratch_for_current_device below) and only that address is
+// handed to kernels.
+static __device__ __align__(256) char scratch[LMH_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -237,9 +245,45 @@ lmh_status_t bwd_impl(const void* hidden, const void* weight, const int32_t* lab
   return launched();
 }
 
+// Device address of `scratch` on the current device, looked up on the first call made on that
+// device and kept (the lookup is idempotent, so racing first calls store the same value).
+constexpr int MAX_DEVICES = 256;
+std::atomic<void*> scratch_ptr[MAX_DEVICES];
+
+lmh_status_t scratch_for_current_device(void*& ptr) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return LMH_ERR_HIP;
+  if (dev < 0 || dev >= MAX_DEVICES) return LMH_ERR_UNSUPPORTED;
+  void* p = scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return LMH_ERR_HIP;
+    scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  ptr = p;
+  return LMH_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+lmh_status_t lmhead_logprob_fwd_noalloc(const void* hidden, const void* weight, const int32_t* labels, int64_t T,
+                                        int64_t H, int64_t V, float* logprob, float* entropy, float* lse,
+                                        hipStream_t stream) {
+  LMH_TRY(check_sizes(T, H, V));
+  if (T == 0) return LMH_OK;
+  LMH_TRY(check_inputs(hidden, weight, labels));
+  LMH_TRY(check_out(logprob, true));
+  LMH_TRY(check_out(entropy, false));
+  LMH_TRY(check_out(lse, false));
+  const size_t need = fwd_ws(T, V).total;
+  if (need > (size_t)LMH_NOALLOC_SCRATCH_BYTES) return LMH_ERR_WORKSPACE_TOO_SMALL;
+  void* ws = nullptr;
+  LMH_TRY(scratch_for_current_device(ws));
+  // the tile counters in the scratch are reset by a kernel inside the call, and every other word
+  // the call reads is written by it first, so the previous call's contents do not matter
+  return fwd_impl(hidden, weight, labels, T, H, V, 1.0f, logprob, entropy, lse, nullptr, ws, need, stream);
+}
 
 size_t lmhead_logprob_fwd_workspace_size(int64_t T, int64_t H, int64_t V) {
   if (check_sizes(T, H, V) != LMH_OK) return 0;

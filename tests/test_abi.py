@@ -174,3 +174,21 @@ def test_extended_entry_validation_codes(lib):
     assert bwd_ex(1.0, vs=max_v - 11, gh=None, gw=None) == lmh.LMH_OK
     assert bwd_ex(1.0, vs=77, gh=None, gw=None) == lmh.LMH_OK        # any start: no records are written
 
+
+def test_noalloc_validation_codes(lib):
+    # refused on the host before the device is touched: sizes past the built-in scratch, bad sizes,
+    # null or misaligned pointers (fake, never-dereferenced addresses)
+    def call(hidden=16, weight=16, labels=16, T=4, H=8, V=10, logprob=16):
+        return lib.lmhead_logprob_fwd_noalloc(hidden, weight, labels, T, H, V, logprob, None, None, None)
+    V = 152064
+    T = 1
+    while lmh.lmhead_logprob_fwd_workspace_size(T + 1, 8, V) <= lmh.NOALLOC_SCRATCH_BYTES:
+        T += 1
+    assert call(T=T + 1, V=V) == lmh.LMH_ERR_WORKSPACE_TOO_SMALL
+    assert call(T=1 << 30, V=V) == lmh.LMH_ERR_UNSUPPORTED             # past 2^36 record slots
+    assert call(T=0) == lmh.LMH_OK
+    assert call(hidden=None) == lmh.LMH_ERR_INVALID_ARG
+    assert call(logprob=None) == lmh.LMH_ERR_INVALID_ARG
+    assert call(weight=8) == lmh.LMH_ERR_UNSUPPORTED
+    assert call(H=12) == lmh.LMH_ERR_UNSUPPORTED
+    assert call(V=0) == lmh.LMH_ERR_INVALID_ARG
