@@ -52,6 +52,9 @@ def parse():
     p.add_argument("--cpu-sample-rows", type=int, default=-1,
                    help="rows of the workload the CPU oracle is timed on (0 disables the CPU baseline; "
                         "-1 sizes the sample to about CPU_TARGET_S seconds of oracle work)")
+    p.add_argument("--bwd-workspace-mb", type=int, default=0,
+                   help="run the backward with a workspace of this many MiB (0: the size of the fastest "
+                        "schedule); the library then takes the widest vocabulary step that fits")
     p.add_argument("--copy-bytes", type=int, default=0,
                    help="also run a plain device copy of this many bytes (counter calibration)")
     return p.parse_args()
@@ -164,7 +167,10 @@ def main():
         ge = x.grad_entropy.to(dev) if x.grad_entropy is not None else None
         gh = torch.empty((T, H), dtype=torch.float32, device=dev)
         gw = torch.empty((V, H), dtype=torch.float32, device=dev)
-        wsb = torch.empty(lmh.lmhead_logprob_bwd_workspace_size(T, H, V), dtype=torch.uint8, device=dev)
+        wsb_bytes = lmh.lmhead_logprob_bwd_workspace_size(T, H, V)
+        if a.bwd_workspace_mb:
+            wsb_bytes = a.bwd_workspace_mb << 20
+        wsb = torch.empty(wsb_bytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     extended = tau != 1.0 or wl.sum_p2 or wl.shards > 1 or wl.entropy_grad
     if wl.shards > 1:   # every shard's records, once, so the fold reads real data
@@ -255,6 +261,7 @@ def main():
                    "backward": bool(wl.backward),
                    **({"temperature": tau} if tau != 1.0 else {}), **({"sum_p2": True} if wl.sum_p2 else {}),
                    **({"entropy_grad": True} if wl.entropy_grad else {}),
+                   **({"bwd_workspace_bytes": wsb_bytes} if wl.backward else {}),
                    **({"vocab_shard": [v0, v1], "shards": wl.shards} if wl.shards > 1 else {})},
         "tflops": flops / (ms * 1e-3) / 1e12,
         "pct_bf16_mfma_peak": 100.0 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,

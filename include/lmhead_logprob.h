@@ -101,8 +101,19 @@ LMH_API lmh_status_t lmhead_logprob_fwd_finalize(const int32_t* labels, int64_t 
                                                  float* logprob, float* entropy, float* lse,
                                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Bytes of workspace lmhead_logprob_bwd needs.  Returns 0 for invalid sizes. */
+/* Bytes of workspace for lmhead_logprob_bwd's fastest schedule.  Returns 0 for invalid sizes.
+ * The backward walks the vocabulary in steps; per step it keeps dz in bf16 twice (token-major and
+ * vocabulary-major, 4 * T bytes per vocabulary row) and the step's weight rows transposed, plus the
+ * transposed hidden once (2 * H * T bytes).  The fastest step is 65536 rows (about 1.8 GB at
+ * T = 4096, H = 5120).  A smaller workspace is accepted down to the size for a 256-row step
+ * (lmhead_logprob_bwd_workspace_size_step(T, H, V, 256)): the call then takes a step, a multiple
+ * of 256 rows whose buffers fit the bytes given (the widest, or one down to half as wide that
+ * keeps the compute units busier).  The results are the same bits for every step width. */
 LMH_API size_t lmhead_logprob_bwd_workspace_size(int64_t T, int64_t H, int64_t V);
+
+/* Bytes of workspace the backward needs with a vocabulary step of `step` rows (rounded up to a
+ * multiple of 256, at most 65536).  Returns 0 for invalid sizes or step <= 0. */
+LMH_API size_t lmhead_logprob_bwd_workspace_size_step(int64_t T, int64_t H, int64_t V, int64_t step);
 
 /* Backward of sum_t grad_logprob_t * logprob_t (entropy has no gradient).
  * dz_tj = g_t * ([j == y_t] - exp(z_tj - lse_t)), the logits being recomputed (SkyRL PR #1765:

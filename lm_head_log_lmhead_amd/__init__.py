@@ -36,6 +36,7 @@ _SIGNATURES = {
     "lmhead_logprob_fwd_partials": (_INT, [_P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P]),
     "lmhead_logprob_fwd_finalize": (_INT, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P]),
     "lmhead_logprob_bwd_workspace_size": (_SZ, [_I64, _I64, _I64]),
+    "lmhead_logprob_bwd_workspace_size_step": (_SZ, [_I64, _I64, _I64, _I64]),
     "lmhead_logprob_bwd": (_INT, [_P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _INT, _P, _SZ, _P]),
     "lmhead_logprob_fwd_ex": (_INT, [_P, _P, _P, _I64, _I64, _I64, _F, _P, _P, _P, _P, _P, _SZ, _P]),
     "lmhead_logprob_fwd_partials_ex": (_INT, [_P, _P, _P, _I64, _I64, _I64, _F, _I64, _I64, _INT, _P, _SZ, _P]),
@@ -118,6 +119,10 @@ def lmhead_logprob_fwd_workspace_size(T: int, H: int, V: int) -> int:
 
 def lmhead_logprob_bwd_workspace_size(T: int, H: int, V: int) -> int:
     return int(lib().lmhead_logprob_bwd_workspace_size(T, H, V))
+
+
+def lmhead_logprob_bwd_workspace_size_step(T: int, H: int, V: int, step: int) -> int:
+    return int(lib().lmhead_logprob_bwd_workspace_size_step(T, H, V, step))
 
 
 def _dims(hidden: torch.Tensor, weight: torch.Tensor):

@@ -202,6 +202,42 @@ lmh_status_t fwd_impl(const void* hidden, const void* weight, const int32_t* lab
   return launched();
 }
 
+// Rounds of dz tiles (256 x 256, one per CU at a time) the backward runs with a step of `step`
+// vocabulary rows: the measure of time used to pick among the steps that fit a workspace.
+int64_t bwd_dz_rounds(int64_t T, int64_t V, int64_t step, int cus) {
+  const int64_t nt = (T + 255) / 256;
+  const int64_t full = V / step, rest = V % step;
+  const int64_t per_step = ((step + 255) / 256 * nt + cus - 1) / cus;
+  return full * per_step + (rest ? ((rest + 255) / 256 * nt + cus - 1) / cus : 0);
+}
+
+// The backward's layout for a workspace of `bytes`: the widest vocabulary step (a multiple of
+// BWD_STEP_UNIT, at most BWD_VOCAB_STEP) whose buffers fit when that is the fastest schedule's;
+// otherwise, among the steps that fit down to half the widest, the one with the fewest rounds of
+// dz tiles on `cus` compute units (a step whose tiles fill the last round of every step beats a
+// slightly wider one that leaves it nearly empty).  False if not even the narrowest step fits.
+// The layout's total grows with the step, so the widest fit is found by bisection.  No result
+// depends on the step.
+bool bwd_choose_layout(int64_t T, int64_t H, int64_t V, size_t bytes, int cus, lmh::BwdLayout& L) {
+  L = lmh::bwd_layout(T, H, V, lmh::BWD_VOCAB_STEP);
+  if (L.total <= bytes) return true;
+  constexpr int64_t U = lmh::BWD_STEP_UNIT;
+  int64_t lo = 1, hi = lmh::BWD_VOCAB_STEP / U;  // in units of BWD_STEP_UNIT
+  if (lmh::bwd_layout(T, H, V, lo * U).total > bytes) return false;
+  while (lo < hi) {
+    const int64_t mid = (lo + hi + 1) / 2;
+    if (lmh::bwd_layout(T, H, V, mid * U).total <= bytes)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  int64_t best = lo;
+  for (int64_t u = lo - 1; u >= 1 && 2 * u >= lo; --u)
+    if (bwd_dz_rounds(T, V, u * U, cus) < bwd_dz_rounds(T, V, best * U, cus)) best = u;
+  L = lmh::bwd_layout(T, H, V, best * U);
+  return true;
+}
+
 lmh_status_t bwd_impl(const void* hidden, const void* weight, const int32_t* labels, int64_t T, int64_t H, int64_t V,
                       float temperature, int64_t vocab_start, const float* grad_logprob, const float* lse,
                       const float* grad_entropy, const float* entropy, float* grad_hidden, float* grad_weight,
@@ -221,11 +257,13 @@ lmh_status_t bwd_impl(const void* hidden, const void* weight, const int32_t* lab
   }
   LMH_TRY(check_out(grad_hidden, false));
   LMH_TRY(check_out(grad_weight, false));
-  const lmh::BwdLayout L = lmh::bwd_layout(T, H, V);
-  LMH_TRY(check_ws(workspace, workspace_bytes, L.total));
+  // any workspace down to the narrowest step's is accepted (the step is chosen below)
+  LMH_TRY(check_ws(workspace, workspace_bytes, lmh::bwd_layout(T, H, V, lmh::BWD_STEP_UNIT).total));
   if (!grad_hidden && !grad_weight) return LMH_OK;
   lmh::BwdArgs a;
   LMH_TRY(device_cus(a.cus));
+  lmh::BwdLayout L;
+  if (!bwd_choose_layout(T, H, V, workspace_bytes, a.cus, L)) return LMH_ERR_WORKSPACE_TOO_SMALL;
   (void)hipGetLastError();
   a.hidden = static_cast<const __bf16*>(hidden);
   a.weight = static_cast<const __bf16*>(weight);
@@ -333,7 +371,14 @@ lmh_status_t lmhead_logprob_fwd_ex(const void* hidden, const void* weight, const
 
 size_t lmhead_logprob_bwd_workspace_size(int64_t T, int64_t H, int64_t V) {
   if (check_sizes(T, H, V) != LMH_OK) return 0;
-  return lmh::bwd_layout(T, H, V).total;
+  return lmh::bwd_layout(T, H, V, lmh::BWD_VOCAB_STEP).total;
+}
+
+size_t lmhead_logprob_bwd_workspace_size_step(int64_t T, int64_t H, int64_t V, int64_t step) {
+  if (check_sizes(T, H, V) != LMH_OK || step <= 0) return 0;
+  step = (step + lmh::BWD_STEP_UNIT - 1) / lmh::BWD_STEP_UNIT * lmh::BWD_STEP_UNIT;
+  if (step > lmh::BWD_VOCAB_STEP) step = lmh::BWD_VOCAB_STEP;
+  return lmh::bwd_layout(T, H, V, step).total;
 }
 
 lmh_status_t lmhead_logprob_bwd(const void* hidden, const void* weight, const int32_t* labels, int64_t T, int64_t H,

@@ -36,7 +36,6 @@ __device__ __forceinline__ void st_dz(__bf16* p, u32x4 v) {
 }
 
 constexpr int DZ_PITCH = WAVE_M * 2 + 16;  // bytes per staged token row (padded against conflicts)
-constexpr int BWD_SCHED_WORDS = 16;        // tile counters per vocabulary step (one per XCD)
 
 // dz of a wavefront's tile part: the lane's four consecutive entries 16 m + 4 g4 + (0..3) of token
 // n * 16 + j, rounded to bf16 and staged token-major in LDS at wl.  dz = g (onehot - p) is formed as
@@ -109,8 +108,12 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void bwd_dz_kernel(
     const __bf16* __restrict__ hidden, const __bf16* __restrict__ weight, const int* __restrict__ labels,
     const float* __restrict__ grad, const float* __restrict__ lse, const float* __restrict__ grad_entropy,
     const float* __restrict__ entropy, float temperature, int T, int H, int V, int vocab_start, int vs0, int Vc,
-    int Vs, int n_mt, int n_nt, __bf16* __restrict__ dz, __bf16* __restrict__ dzt, int ldt) {
+    int Vs, int n_mt, int n_nt, __bf16* __restrict__ dz, __bf16* __restrict__ dzt, int ldt,
+    int* __restrict__ gemm_sched) {
   loop_placement_pad<4 + 2 * SCALED + EGRAD>();
+  // the gradient GEMM that follows this launch claims its tiles from these counters; the previous
+  // step's GEMM has finished before this launch starts
+  if (blockIdx.x == 0 && threadIdx.x < BWD_SCHED_WORDS) gemm_sched[threadIdx.x] = 0;
   constexpr int STAGE_OUT = Cfg::NWAVES * Cfg::WAVE_N * DZ_PITCH;
   constexpr int LDS = PingPong<Cfg>::LDS_BYTES > STAGE_OUT ? PingPong<Cfg>::LDS_BYTES : STAGE_OUT;
   __shared__ __attribute__((aligned(1024))) char lds[LDS];
@@ -395,11 +398,6 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void gemm_tn_f32_persistent_kernel(G
   }
 }
 
-__global__ void bwd_sched_reset_kernel(int* __restrict__ sched, int n) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) sched[i] = 0;
-}
-
 template <class Cfg>
 static GemmProblem make_problem(const __bf16* A, int64_t lda, int M, const __bf16* B, int64_t ldb, int N, int K,
                                 float* C, int64_t ldc, int accumulate) {
@@ -423,14 +421,14 @@ static void launch_gemm_tn(const GemmProblem& p0, const GemmProblem& p1, int* sc
 
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-BwdLayout bwd_layout(int64_t T, int64_t H, int64_t V) {
+BwdLayout bwd_layout(int64_t T, int64_t H, int64_t V, int64_t step) {
   BwdLayout L{};
   L.T = (int)T;
   L.H = (int)H;
   L.V = (int)V;
   L.Tp = (int)((T + 63) / 64 * 64);
-  const int64_t vr = (V + 255) / 256 * 256;
-  L.Vs = (int)(vr < BWD_VOCAB_STEP ? vr : BWD_VOCAB_STEP);
+  const int64_t vr = (V + BWD_STEP_UNIT - 1) / BWD_STEP_UNIT * BWD_STEP_UNIT;
+  L.Vs = (int)(vr < step ? vr : step);
   size_t off = 0;
   L.off_dz = off;
   off += align256((size_t)T * L.Vs * 2);
@@ -442,7 +440,7 @@ BwdLayout bwd_layout(int64_t T, int64_t H, int64_t V) {
   off += align256((size_t)H * L.Tp * 2);
   L.nsteps = (int)((V + L.Vs - 1) / L.Vs);
   L.off_sched = off;
-  off += align256((size_t)L.nsteps * BWD_SCHED_WORDS * sizeof(int));
+  off += align256((size_t)BWD_SCHED_WORDS * sizeof(int));
   L.total = off;
   return L;
 }
@@ -457,12 +455,9 @@ void launch_bwd(const BwdArgs& a, hipStream_t stream) {
   __bf16* dzt = reinterpret_cast<__bf16*>(a.ws + L.off_dzt);
   __bf16* wt = reinterpret_cast<__bf16*>(a.ws + L.off_wt);
   __bf16* ht = reinterpret_cast<__bf16*>(a.ws + L.off_ht);
-  int* sched = reinterpret_cast<int*>(a.ws + L.off_sched);
+  // tile counters of the gradient GEMM, zeroed by each step's dz launch
+  int* gemm_sched = reinterpret_cast<int*>(a.ws + L.off_sched);
   if (!a.grad_hidden && !a.grad_weight) return;
-  {
-    const int n = L.nsteps * BWD_SCHED_WORDS;
-    hipLaunchKernelGGL(bwd_sched_reset_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, sched, n);
-  }
   if (a.grad_weight) launch_transpose(a.hidden, L.H, L.T, L.H, ht, L.Tp, L.Tp, stream);
 
   for (int vs0 = 0; vs0 < L.V; vs0 += L.Vs) {
@@ -475,8 +470,7 @@ void launch_bwd(const BwdArgs& a, hipStream_t stream) {
                          : (egrad ? bwd_dz_kernel<CfgDz, false, true> : bwd_dz_kernel<CfgDz, false, false>);
       hipLaunchKernelGGL(kern, dim3(n_mt * n_nt), dim3(CfgDz::NTHREADS), 0, stream, a.hidden, a.weight, a.labels,
                          a.grad, a.lse, a.grad_entropy, a.entropy, a.temperature, L.T, L.H, L.V, a.vocab_start, vs0,
-                         Vc, L.Vs, n_mt,
-                         n_nt, dz, dzt, L.Tp);
+                         Vc, L.Vs, n_mt, n_nt, dz, dzt, L.Tp, gemm_sched);
     }
     // dz^T rows hold tokens up to T rounded up to 8 (zeros past T); the gradient GEMM reads no
     // 16-byte chunk that starts at or past T
@@ -491,7 +485,7 @@ void launch_bwd(const BwdArgs& a, hipStream_t stream) {
     }
     // grad_hidden first: its tiles run K = Vs (four times the grad_weight tiles' K = T at the
     // benchmark sizes), and dispatching the long tiles first lets the short ones fill the tail
-    launch_gemm_tn<CfgGrad>(ph, pw, sched + (vs0 / L.Vs) * BWD_SCHED_WORDS, a.cus, stream);
+    launch_gemm_tn<CfgGrad>(ph, pw, gemm_sched, a.cus, stream);
   }
 }
 

@@ -11,13 +11,18 @@ namespace lmh {
 
 // Vocabulary width of one forward record (one wavefront's M extent).
 constexpr int VOCAB_CHUNK = WAVE_M;
-// Vocabulary rows per backward step (a multiple of the 256-row tile and of the K step).
-// grad_hidden does not depend on it bit-wise: each step continues the previous step's MFMA
-// accumulation chain.
+// Vocabulary rows per backward step: the widest (fastest) step; a smaller workspace takes the
+// widest multiple of BWD_STEP_UNIT that fits.  No result depends on it bit-wise: grad_hidden's MFMA
+// chain continues across steps and step bounds are multiples of the K slice, grad_weight's chain
+// runs over tokens.
 #ifndef LMH_BWD_STEP
 #define LMH_BWD_STEP 65536
 #endif
 constexpr int BWD_VOCAB_STEP = LMH_BWD_STEP;
+constexpr int BWD_STEP_UNIT = 256;
+// Tile counters of the backward's persistent gradient GEMM (one per XCD), zeroed before each
+// step's GEMM by that step's dz launch.
+constexpr int BWD_SCHED_WORDS = 16;
 
 // Words of the forward workspace used by the large-T tile scheduler (one counter per XCD).
 constexpr int SCHED_WORDS = 16;
@@ -49,12 +54,14 @@ void launch_fwd_finalize(const FwdArgs& a, hipStream_t stream);
 struct BwdLayout {
   int T, H, V;
   int Tp;      // T rounded up to 64 (pitch of the transposed token-major buffers)
-  int Vs;      // vocabulary rows per step: min(BWD_VOCAB_STEP, V rounded up to 256)
+  int Vs;      // vocabulary rows per step: min(step, V rounded up to BWD_STEP_UNIT)
   int nsteps;  // ceil(V / Vs)
   size_t off_dz, off_dzt, off_wt, off_ht, off_sched, total;
 };
 
-BwdLayout bwd_layout(int64_t T, int64_t H, int64_t V);
+// Workspace layout for a step of `step` vocabulary rows (a multiple of BWD_STEP_UNIT, at most
+// BWD_VOCAB_STEP); total grows with the step.
+BwdLayout bwd_layout(int64_t T, int64_t H, int64_t V, int64_t step);
 
 struct BwdArgs {
   const __bf16* hidden;

@@ -192,3 +192,31 @@ def test_noalloc_validation_codes(lib):
     assert call(weight=8) == lmh.LMH_ERR_UNSUPPORTED
     assert call(H=12) == lmh.LMH_ERR_UNSUPPORTED
     assert call(V=0) == lmh.LMH_ERR_INVALID_ARG
+
+
+def test_bwd_workspace_step_sizes(lib):
+    T, H, V = 4096, 5120, 152064
+    fast = lmh.lmhead_logprob_bwd_workspace_size(T, H, V)
+    assert lmh.lmhead_logprob_bwd_workspace_size_step(T, H, V, 65536) == fast
+    assert lmh.lmhead_logprob_bwd_workspace_size_step(T, H, V, 10**9) == fast      # clamped to 65536
+    sizes = [lmh.lmhead_logprob_bwd_workspace_size_step(T, H, V, s) for s in range(256, 65537, 256)]
+    assert all(a < b for a, b in zip(sizes, sizes[1:])), "workspace must grow with the step"
+    assert lmh.lmhead_logprob_bwd_workspace_size_step(T, H, V, 1) == sizes[0]       # rounded up to 256
+    assert sizes[0] < 256 << 20 < fast
+    assert lmh.lmhead_logprob_bwd_workspace_size_step(T, H, V, 0) == 0
+    assert lmh.lmhead_logprob_bwd_workspace_size_step(T, 12, V, 256) == 0
+    # a small V needs no more than V rounded up to 256 rows per step
+    assert lmh.lmhead_logprob_bwd_workspace_size_step(64, 64, 300, 65536) == \
+        lmh.lmhead_logprob_bwd_workspace_size_step(64, 64, 300, 512)
+
+
+def test_bwd_accepts_any_workspace_down_to_the_narrowest_step(lib):
+    T, H, V = 300, 64, 5000
+    least = lmh.lmhead_logprob_bwd_workspace_size_step(T, H, V, 256)
+
+    def call(wsb, gh=16, gw=16):
+        return lib.lmhead_logprob_bwd(16, 16, 16, T, H, V, 16, 16, gh, gw, 0, 256, wsb, None)
+
+    assert call(least - 1) == lmh.LMH_ERR_WORKSPACE_TOO_SMALL
+    assert call(least, gh=None, gw=None) == lmh.LMH_OK          # validated; nothing to compute
+    assert call((least + lmh.lmhead_logprob_bwd_workspace_size(T, H, V)) // 2, gh=None, gw=None) == lmh.LMH_OK

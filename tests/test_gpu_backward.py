@@ -76,3 +76,28 @@ def test_grad_weight_split_accumulate_is_bitwise():
         lmh.lmhead_logprob_bwd(hs, w, ys, gs, lse, None, acc, i > 0, ws)
     torch.cuda.synchronize()
     assert np.array_equal(bits(acc), bits(gw))
+
+
+def _bwd_with_workspace(h, w, y, g, lse, nbytes):
+    T, H = h.shape
+    V = w.shape[0]
+    gh = torch.empty((T, H), dtype=torch.float32, device=dev())
+    gw = torch.empty((V, H), dtype=torch.float32, device=dev())
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev())
+    lmh.lmhead_logprob_bwd(h, w, y, g, lse, gh, gw, False, ws)
+    torch.cuda.synchronize()
+    return bits(gh), bits(gw)
+
+
+@pytest.mark.parametrize("T,H,V", [(300, 256, 5000), (40, 64, 140000)])
+def test_step_width_does_not_change_bits(T, H, V):
+    # the workspace decides the vocabulary step (the widest multiple of 256 that fits); every step
+    # width must give the bits of the widest
+    print(f"[case] bwd step widths T={T} H={H} V={V}", flush=True)
+    h, w, y, g = to_dev(*_case(T, H, V, seed=T + 5))
+    _, _, lse = lmh.forward(h, w, y, want_lse=True)
+    ref = _bwd_with_workspace(h, w, y, g, lse, lmh.lmhead_logprob_bwd_workspace_size(T, H, V))
+    for step in (256, 768, 4096, 33024):
+        got = _bwd_with_workspace(h, w, y, g, lse, lmh.lmhead_logprob_bwd_workspace_size_step(T, H, V, step))
+        assert np.array_equal(got[0], ref[0]), f"grad_hidden differs at step {step}"
+        assert np.array_equal(got[1], ref[1]), f"grad_weight differs at step {step}"

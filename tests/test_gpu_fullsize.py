@@ -107,3 +107,13 @@ def test_T4096_H5120_V152064_backward_sampled():
     torch.cuda.synchronize()
     assert np.array_equal(bits(torch.cat(parts)), bits(gh))
     assert np.array_equal(bits(gw2), bits(gw))
+
+    # a 256 MB workspace (a 7936-row vocabulary step instead of 65536) gives the same bits
+    T, H, V = x.hidden.shape[0], x.hidden.shape[1], x.weight.shape[0]
+    assert lmh.lmhead_logprob_bwd_workspace_size(T, H, V) > 256 << 20
+    ws = torch.empty(256 << 20, dtype=torch.uint8, device=dev())
+    gh3 = torch.empty_like(gh)
+    gw3 = torch.empty_like(gw)
+    lmh.lmhead_logprob_bwd(h, w, y, g, lse, gh3, gw3, False, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(gh3), bits(gh)) and np.array_equal(bits(gw3), bits(gw))
