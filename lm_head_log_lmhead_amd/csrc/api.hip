@@ -3,6 +3,7 @@
 #include "lmhead_logprob.h"
 
 #include <math.h>
+#include <string.h>
 
 #include <atomic>
 
@@ -136,7 +137,7 @@ FwdArgs make_fwd_args(const void* hidden, const void* weight, const int32_t* lab
 // vocabulary of vocab_total; shards start on a chunk and all but the last cover whole chunks.
 lmh_status_t check_shard(int64_t V, int64_t vocab_start, int64_t vocab_total) {
   if (V <= 0 || vocab_start < 0 || vocab_total <= 0) return LMH_ERR_INVALID_ARG;
-  if (vocab_start + V > vocab_total) return LMH_ERR_INVALID_ARG;
+  if (vocab_start > vocab_total - V) return LMH_ERR_INVALID_ARG;  // vocab_start + V > vocab_total, without overflow
   if (vocab_start % lmh::VOCAB_CHUNK != 0) return LMH_ERR_UNSUPPORTED;
   if (V % lmh::VOCAB_CHUNK != 0 && vocab_start + V != vocab_total) return LMH_ERR_UNSUPPORTED;
   return LMH_OK;
@@ -245,7 +246,7 @@ lmh_status_t bwd_impl(const void* hidden, const void* weight, const int32_t* lab
   LMH_TRY(check_sizes(T, H, V));
   if (accumulate_grad_weight != 0 && accumulate_grad_weight != 1) return LMH_ERR_INVALID_ARG;
   LMH_TRY(check_temperature(temperature));
-  if (vocab_start < 0 || vocab_start + V >= MAX_V) return LMH_ERR_INVALID_ARG;
+  if (vocab_start < 0 || vocab_start >= MAX_V - V) return LMH_ERR_INVALID_ARG;  // V < MAX_V checked above
   if (T >= MAX_T_BWD) return LMH_ERR_UNSUPPORTED;
   if (T == 0) return LMH_OK;  // no rows: nothing is launched and the gradient buffers are untouched
   LMH_TRY(check_inputs(hidden, weight, labels));
@@ -376,8 +377,8 @@ size_t lmhead_logprob_bwd_workspace_size(int64_t T, int64_t H, int64_t V) {
 
 size_t lmhead_logprob_bwd_workspace_size_step(int64_t T, int64_t H, int64_t V, int64_t step) {
   if (check_sizes(T, H, V) != LMH_OK || step <= 0) return 0;
+  if (step > lmh::BWD_VOCAB_STEP) step = lmh::BWD_VOCAB_STEP;  // clamped first: no overflow rounding up
   step = (step + lmh::BWD_STEP_UNIT - 1) / lmh::BWD_STEP_UNIT * lmh::BWD_STEP_UNIT;
-  if (step > lmh::BWD_VOCAB_STEP) step = lmh::BWD_VOCAB_STEP;
   return lmh::bwd_layout(T, H, V, step).total;
 }
 
@@ -400,7 +401,11 @@ lmh_status_t lmhead_logprob_bwd_ex(const void* hidden, const void* weight, const
 }
 
 const char* lmhead_status_string(lmh_status_t s) {
-  switch (s) {
+  // A C caller may pass any int; its bytes are read as an int, not as the enum (whose C++ range
+  // covers only the listed codes).
+  int code;
+  memcpy(&code, &s, sizeof code);
+  switch (code) {
     case LMH_OK: return "ok";
     case LMH_ERR_INVALID_ARG: return "invalid argument (null required pointer, non-positive size or temperature)";
     case LMH_ERR_UNSUPPORTED: return "unsupported (H % 8 != 0, a size limit, a misaligned pointer or shard)";
