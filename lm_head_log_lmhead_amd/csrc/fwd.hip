@@ -480,6 +480,50 @@ __global__ __launch_bounds__(64 * FIN_WAVES) void fwd_finalize_kernel(FwdArgs a,
   }
 }
 
+// Small T: one wavefront per token, lane s folding segment s (the lane layout of the tree above),
+// so the T rows' folds spread over T wavefronts instead of the few workgroups of
+// fwd_finalize_kernel (one workgroup, one CU, at T <= 16).  Same segments, same ascending order
+// inside a segment, same tree: the same bits.
+constexpr int FINW_WAVES = 4;  // wavefronts (tokens) per workgroup
+
+template <bool P2>
+__global__ __launch_bounds__(64 * FINW_WAVES) void fwd_finalize_wave_kernel(FwdArgs a, int n_c) {
+  constexpr int BATCH = 20;  // one batch covers a segment of V <= 163840
+  const int T = a.T;
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * FINW_WAVES + (threadIdx.x >> 6);
+  if (t >= T) return;  // the whole wavefront
+  const int lo = (int)((int64_t)lane * n_c / FIN_NSEG);
+  const int len = (int)((int64_t)(lane + 1) * n_c / FIN_NSEG) - lo;
+  Rec st{-__builtin_inff(), 0.f, 0.f, 0.f, 0.f};
+  for (int b = 0; b < len; b += BATCH) {
+    f32x4 r[BATCH];
+    float r2[BATCH];
+#pragma unroll
+    for (int i = 0; i < BATCH; ++i) {
+      const int c = b + i;
+      const bool ok = c < len;
+      const size_t at = (size_t)(lo + c) * (size_t)T + t;
+      r[i] = ok ? a.rec[at] : (f32x4)(0.f);
+      r2[i] = (P2 && ok) ? (a.p2ok[lo + c] ? a.rec2[at] : __builtin_nanf("")) : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < BATCH; ++i) st = fold<P2>(st, Rec{r[i][0], r[i][1], r[i][2], r[i][3], r2[i]});
+  }
+#pragma unroll
+  for (int d = 1; d < FIN_NSEG; d *= 2) {
+    Rec o;
+    o.m = __shfl_down(st.m, d);
+    o.n = __shfl_down(st.n, d);
+    o.b = __shfl_down(st.b, d);
+    o.u = __shfl_down(st.u, d);
+    o.q = P2 ? __shfl_down(st.q, d) : 0.f;
+    const Rec f = fold<P2>(st, o);
+    if ((lane & (2 * d - 1)) == 0) st = f;
+  }
+  if (lane == 0) finalize_row<P2>(a, t, st);
+}
+
 // ---------------------------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------------------------
@@ -563,8 +607,20 @@ static void launch_finalize_tpw(const FwdArgs& a, int n_c, hipStream_t stream) {
     hipLaunchKernelGGL((fwd_finalize_kernel<false, TPW>), grid, dim3(64 * FIN_WAVES), 0, stream, a, n_c, nblk);
 }
 
+#ifndef LMH_FINW_MAX_T
+#define LMH_FINW_MAX_T 256
+#endif
+
 void launch_fwd_finalize(const FwdArgs& a, hipStream_t stream) {
   const int n_c = (a.vocab_total + WAVE_M - 1) / WAVE_M;
+  if (a.T <= LMH_FINW_MAX_T) {
+    const dim3 grid((a.T + FINW_WAVES - 1) / FINW_WAVES);
+    if (a.sum_p2)
+      hipLaunchKernelGGL(fwd_finalize_wave_kernel<true>, grid, dim3(64 * FINW_WAVES), 0, stream, a, n_c);
+    else
+      hipLaunchKernelGGL(fwd_finalize_wave_kernel<false>, grid, dim3(64 * FINW_WAVES), 0, stream, a, n_c);
+    return;
+  }
   if (a.T <= 2048)
     launch_finalize_tpw<16>(a, n_c, stream);
   else

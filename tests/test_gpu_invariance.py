@@ -120,3 +120,19 @@ def test_repeat_run_identity(data, reference):
     for _ in range(3):
         lp, ent, lse = fwd_raw(data["probes"], data["w"], data["py"])
         assert np.array_equal(_outs(lp, ent, lse), reference[0])
+
+
+@pytest.mark.parametrize("tau,p2", [(1.0, False), (0.7, True)])
+def test_wave_fold_equals_block_fold(tau, p2):
+    # T <= 256 folds one wavefront per row, larger T folds in row blocks: the same rows, alone and
+    # inside a batch of 700, give the same bits (with a temperature and sum_p2 too)
+    import lm_head_log_lmhead_amd as lmh
+    H, V = 264, 20000
+    x = synth.make_inputs(700, H, V, seed=31, weight_std=0.05)
+    h, w, y = x.hidden.to(dev()), x.weight.to(dev()), x.labels.to(dev())
+    big = lmh.forward(h, w, y, entropy=True, want_lse=True, temperature=tau, sum_p2=p2)
+    for s0, s1 in ((0, 1), (5, 21), (100, 356), (400, 600)):
+        part = lmh.forward(h[s0:s1], w, y[s0:s1], entropy=True, want_lse=True, temperature=tau, sum_p2=p2)
+        torch.cuda.synchronize()
+        for k in range(len(part)):
+            assert np.array_equal(bits(part[k]), bits(big[k][s0:s1])), f"rows [{s0}, {s1}) output {k}"
