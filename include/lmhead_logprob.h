@@ -70,16 +70,26 @@ typedef enum {
   LMH_OK = 0,
   LMH_ERR_INVALID_ARG = 1,          /* null required pointer, negative or zero size           */
   LMH_ERR_UNSUPPORTED = 2,          /* H % 8 != 0, size limits, misaligned pointer              */
-  LMH_ERR_WORKSPACE_TOO_SMALL = 3,  /* workspace_bytes below the *_workspace_size() value       */
+  LMH_ERR_WORKSPACE_TOO_SMALL = 3,  /* workspace_bytes below the smallest accepted size          */
   LMH_ERR_HIP = 4                   /* a kernel launch failed (hipGetLastError after launching) */
 } lmh_status_t;
 
-/* Bytes of workspace lmhead_logprob_fwd needs (also the stage entry points below).  Returns 0 for
- * invalid sizes.  The workspace holds one 20-byte record per (row, 128-column vocabulary chunk),
- * one float per row, 256 bytes of tile-scheduler counters and one int per chunk; its initial
- * contents do not matter.
+/* Bytes of workspace for the fastest lmhead_logprob_fwd (also the stage entry points below).
+ * Returns 0 for invalid sizes.  The workspace holds one 20-byte record per (row, 128-column
+ * vocabulary chunk), one float per row, 256 bytes of tile-scheduler counters and one int per
+ * chunk.  Where the call has one 256-token tile and few 256-row vocabulary tiles per compute unit
+ * (192 <= T <= 256 and 256 < ceil(V / 256) < 1024, e.g. T = 256 at V = 152064) it also holds
+ * 64 MiB of accumulator slots and 1 KiB of flags, with which the partials stage splits the tiles'
+ * K loops evenly over the compute units (same bits as without).  The initial contents do not
+ * matter.
  * Calls that may run concurrently need separate workspaces. */
 LMH_API size_t lmhead_logprob_fwd_workspace_size(int64_t T, int64_t H, int64_t V);
+
+/* The smallest forward workspace the calls accept: lmhead_logprob_fwd_workspace_size without the
+ * accumulator slots and flags (equal to it where those do not apply).  Any workspace_bytes from
+ * this size up is accepted; below lmhead_logprob_fwd_workspace_size the partials stage runs
+ * without the K split (the same bits, more time at few tiles per compute unit). */
+LMH_API size_t lmhead_logprob_fwd_workspace_size_min(int64_t T, int64_t H, int64_t V);
 
 /* Forward.  logprob is required; entropy and lse may be NULL (not computed / not written).
  * lse is what lmhead_logprob_bwd needs later. */
@@ -206,7 +216,7 @@ LMH_API lmh_status_t lmhead_logprob_bwd_ex(const void* hidden, const void* weigh
  * lmhead_logprob_fwd (the same kernels, so the same bits) without the workspace: the library
  * keeps one built-in scratch array of LMH_NOALLOC_SCRATCH_BYTES per device, which each device
  * holds until the process ends.  The call makes no allocation of any kind.
- * Limit: lmhead_logprob_fwd_workspace_size(T, H, V) <= LMH_NOALLOC_SCRATCH_BYTES (20 bytes per
+ * Limit: lmhead_logprob_fwd_workspace_size_min(T, H, V) <= LMH_NOALLOC_SCRATCH_BYTES (20 bytes per
  * row and 128-row vocabulary chunk, about T * ceil(V / 128) <= 3.3e6, e.g. T <= 2823 at
  * V = 152064); larger calls return LMH_ERR_WORKSPACE_TOO_SMALL with nothing launched.
  * Every call on a device uses that device's one array: calls that may overlap on one device (on

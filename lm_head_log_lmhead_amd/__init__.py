@@ -32,6 +32,7 @@ _F = ctypes.c_float
 _INT = ctypes.c_int
 _SIGNATURES = {
     "lmhead_logprob_fwd_workspace_size": (_SZ, [_I64, _I64, _I64]),
+    "lmhead_logprob_fwd_workspace_size_min": (_SZ, [_I64, _I64, _I64]),
     "lmhead_logprob_fwd": (_INT, [_P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P]),
     "lmhead_logprob_fwd_partials": (_INT, [_P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P]),
     "lmhead_logprob_fwd_finalize": (_INT, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P]),
@@ -115,6 +116,10 @@ def lmhead_status_string(status: int) -> str:
 
 def lmhead_logprob_fwd_workspace_size(T: int, H: int, V: int) -> int:
     return int(lib().lmhead_logprob_fwd_workspace_size(T, H, V))
+
+
+def lmhead_logprob_fwd_workspace_size_min(T: int, H: int, V: int) -> int:
+    return int(lib().lmhead_logprob_fwd_workspace_size_min(T, H, V))
 
 
 def lmhead_logprob_bwd_workspace_size(T: int, H: int, V: int) -> int:

@@ -57,7 +57,7 @@ def hipcc() -> str:
 
 # ---- loop placement ---------------------------------------------------------------------------
 
-N_LOOP_KERNELS = 9
+N_LOOP_KERNELS = 13
 LOOP_TARGET = 4        # bytes past a LOOP_GRANULE boundary
 LOOP_GRANULE = 32
 
@@ -72,6 +72,9 @@ def _kernel_id(symbol: str):
         return 4 + 2 * int(m.group(1)) + int(m.group(2))
     if "gemm_tn_f32_persistent_kernel" in symbol:
         return 8
+    m = re.search(r"fwd_partials_sk_kernel.*RecOptILb(\d)ELb(\d)E", symbol)
+    if m:
+        return 9 + 2 * int(m.group(1)) + int(m.group(2))
     return None
 
 

@@ -45,11 +45,14 @@ lmh_status_t check_sizes(int64_t T, int64_t H, int64_t V) {
 
 struct FwdWs {
   size_t rec_off, rec2_off, zy_off, sched_off, p2ok_off, total;
+  size_t sk_sync_off, sk_acc_off, total_sk;
 };
 
 // Forward workspace for a vocabulary of V rows: records and squared-sum records for every
 // 128-row chunk, label logits, tile counters, and one flag per chunk telling whether its
-// squared-sum records were written.
+// squared-sum records were written (total bytes: the least every forward call accepts).  Past
+// that, the K-split schedule's counter, flags and accumulator slots (total_sk); a partials call
+// whose workspace holds them runs that schedule where it applies.
 FwdWs fwd_ws(int64_t T, int64_t V) {
   const int64_t n_c = (V + lmh::VOCAB_CHUNK - 1) / lmh::VOCAB_CHUNK;
   FwdWs w;
@@ -59,7 +62,17 @@ FwdWs fwd_ws(int64_t T, int64_t V) {
   w.sched_off = w.zy_off + align256((size_t)T * 4);
   w.p2ok_off = w.sched_off + align256(lmh::SCHED_WORDS * sizeof(int));
   w.total = w.p2ok_off + align256((size_t)n_c * sizeof(int));
+  w.sk_sync_off = w.total;
+  w.sk_acc_off = w.sk_sync_off + align256(lmh::SK_SYNC_WORDS * sizeof(int));
+  w.total_sk = w.sk_acc_off + (size_t)lmh::SK_MAX_WG * lmh::SK_SLOT_BYTES;
   return w;
+}
+
+// The workspace size that gives the fastest schedule (the K-split one where it applies on a
+// device of SK_MAX_WG compute units).
+size_t fwd_ws_fast(int64_t T, int64_t V) {
+  const FwdWs w = fwd_ws(T, V);
+  return lmh::fwd_sk_wanted(T, V, lmh::SK_MAX_WG) ? w.total_sk : w.total;
 }
 
 lmh_status_t check_inputs(const void* hidden, const void* weight, const int32_t* labels) {
@@ -100,7 +113,8 @@ lmh_status_t device_cus(int& cus) {
 
 FwdArgs make_fwd_args(const void* hidden, const void* weight, const int32_t* labels, int64_t T, int64_t H,
                       int64_t V, int64_t vocab_start, int64_t vocab_total, float temperature, int want_p2,
-                      float* logprob, float* entropy, float* lse, float* sum_p2, void* workspace) {
+                      float* logprob, float* entropy, float* lse, float* sum_p2, void* workspace,
+                      size_t workspace_bytes) {
   const FwdWs w = fwd_ws(T, vocab_total);
   char* ws = static_cast<char*>(workspace);
   FwdArgs a;
@@ -119,6 +133,9 @@ FwdArgs make_fwd_args(const void* hidden, const void* weight, const int32_t* lab
   a.zy = reinterpret_cast<float*>(ws + w.zy_off);
   a.sched = reinterpret_cast<int*>(ws + w.sched_off);
   a.p2ok = reinterpret_cast<int*>(ws + w.p2ok_off);
+  const bool sk_room = workspace_bytes >= w.total_sk;
+  a.sk_sync = sk_room ? reinterpret_cast<int*>(ws + w.sk_sync_off) : nullptr;
+  a.sk_acc = sk_room ? reinterpret_cast<lmh::f32x4*>(ws + w.sk_acc_off) : nullptr;
   a.logprob = logprob;
   a.entropy = entropy;
   a.lse = lse;
@@ -154,7 +171,7 @@ lmh_status_t fwd_partials_impl(const void* hidden, const void* weight, const int
   LMH_TRY(check_inputs(hidden, weight, labels));
   LMH_TRY(check_ws(workspace, workspace_bytes, fwd_ws(T, vocab_total).total));
   FwdArgs a = make_fwd_args(hidden, weight, labels, T, H, V, vocab_start, vocab_total, temperature, want_sum_p2,
-                            nullptr, nullptr, nullptr, nullptr, workspace);
+                            nullptr, nullptr, nullptr, nullptr, workspace, workspace_bytes);
   LMH_TRY(device_cus(a.cus));
   (void)hipGetLastError();  // clear any stale error so the check after launching sees only ours
   lmh::launch_fwd_partials(a, stream);
@@ -176,7 +193,7 @@ lmh_status_t fwd_finalize_impl(const int32_t* labels, int64_t T, int64_t H, int6
   (void)hipGetLastError();
   lmh::launch_fwd_finalize(
       make_fwd_args(nullptr, nullptr, labels, T, H, V, 0, V, 1.0f, sum_p2 != nullptr, logprob, entropy, lse, sum_p2,
-                    workspace),
+                    workspace, workspace_bytes),
       stream);
   return launched();
 }
@@ -194,7 +211,7 @@ lmh_status_t fwd_impl(const void* hidden, const void* weight, const int32_t* lab
   LMH_TRY(check_out(sum_p2, false));
   LMH_TRY(check_ws(workspace, workspace_bytes, fwd_ws(T, V).total));
   FwdArgs a = make_fwd_args(hidden, weight, labels, T, H, V, 0, V, temperature, sum_p2 != nullptr, logprob, entropy,
-                            lse, sum_p2, workspace);
+                            lse, sum_p2, workspace, workspace_bytes);
   LMH_TRY(device_cus(a.cus));
   (void)hipGetLastError();
   lmh::launch_fwd_partials(a, stream);
@@ -319,12 +336,19 @@ lmh_status_t lmhead_logprob_fwd_noalloc(const void* hidden, const void* weight, 
   if (need > (size_t)LMH_NOALLOC_SCRATCH_BYTES) return LMH_ERR_WORKSPACE_TOO_SMALL;
   void* ws = nullptr;
   LMH_TRY(scratch_for_current_device(ws));
-  // the tile counters in the scratch are reset by a kernel inside the call, and every other word
-  // the call reads is written by it first, so the previous call's contents do not matter
-  return fwd_impl(hidden, weight, labels, T, H, V, 1.0f, logprob, entropy, lse, nullptr, ws, need, stream);
+  // the tile counters (and the K-split schedule's counter and flags) in the scratch are reset by a
+  // kernel inside the call, and every other word the call reads is written by it first, so the
+  // previous call's contents do not matter
+  return fwd_impl(hidden, weight, labels, T, H, V, 1.0f, logprob, entropy, lse, nullptr, ws,
+                  (size_t)LMH_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 size_t lmhead_logprob_fwd_workspace_size(int64_t T, int64_t H, int64_t V) {
+  if (check_sizes(T, H, V) != LMH_OK) return 0;
+  return fwd_ws_fast(T, V);
+}
+
+size_t lmhead_logprob_fwd_workspace_size_min(int64_t T, int64_t H, int64_t V) {
   if (check_sizes(T, H, V) != LMH_OK) return 0;
   return fwd_ws(T, V).total;
 }

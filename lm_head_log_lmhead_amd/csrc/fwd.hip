@@ -327,6 +327,186 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void fwd_partials_persistent_kernel(
   }
 }
 
+// K-split form for launches of few tile rounds (one workgroup per CU).
+//
+// With few tiles per CU the dynamic queue leaves a partly empty last round: at T = 256 and
+// V = 152064, 594 tiles on 256 CUs are 2.32 rounds, and a third of the CUs run a third tile while
+// the rest idle.  Here the K steps of all tiles, in tile order, are cut into one contiguous range
+// per workgroup of equal length, so every workgroup has the same number of steps.  A range starts
+// inside a tile (its "tail": steps kb .. S-1), covers whole tiles, and ends inside another (its
+// "head": steps 0 .. ke-1), whose tail is the next workgroup's first part.  A workgroup computes
+// its head first and hands the accumulators to the next workgroup through the workspace; it
+// computes its own tail last, continuing the accumulators the previous workgroup handed over.
+// The chain of every output element is the same as in one piece: the same MFMAs over the same
+// k slices in ascending order, the fp32 accumulators stored and loaded exactly in between.
+//
+// Workgroup numbers come from a counter taken at start, so the workgroup a tail waits for took
+// its number earlier and is running; it computes its head before anything else, so every wait
+// ends.  The hand-over uses coherent (sc1) stores and loads, which the XCDs' separate L2 caches
+// serve consistently: the writer's stores complete before it sets the flag, and the reader loads
+// the accumulators only after it has seen the flag.  The counter and flags are zeroed by
+// fwd_sk_reset_kernel before the launch.
+
+__global__ void fwd_sk_reset_kernel(int* __restrict__ sync, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) sync[i] = 0;
+}
+
+struct SkPiece {
+  int L, k0, k1;  // tile and its K steps [k0, k1)
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t sk_slot(const FwdArgs& a, int g) {
+  return __builtin_amdgcn_make_buffer_rsrc(a.sk_acc + (size_t)g * (SK_SLOT_BYTES / 16), 0, (int)SK_SLOT_BYTES,
+                                          0x00020000);
+}
+constexpr int SC1 = 16;  // cache policy of the hand-over: coherent across the XCDs
+
+template <class Cfg, class Opt>
+__global__ __launch_bounds__(Cfg::NTHREADS) void fwd_partials_sk_kernel(FwdArgs a, int n_mt, int n_nt) {
+  loop_placement_pad<9 + 2 * Opt::SCALED + Opt::P2>();
+  __shared__ __attribute__((aligned(1024))) char lds[Cfg::LDS_BYTES];
+  int* const bc = reinterpret_cast<int*>(lds + PingPong<Cfg>::B_BASE + PingPong<Cfg>::SLOT);
+  const int tid = threadIdx.x;
+  const int wm = (tid >> 6) % Cfg::WM;
+  const int wn = (tid >> 6) / Cfg::WM;
+  const int lane = tid & 63;
+  const int H = a.H;
+  const int S = (H + Cfg::BK - 1) / Cfg::BK;  // K steps of a tile
+  const int G = gridDim.x;
+
+  if (tid == 0) bc[0] = atomicAdd(a.sk_sync, 1);
+  __syncthreads();
+  const int g = bc[0];
+  const int64_t U = (int64_t)n_mt * n_nt * S;
+  // This workgroup's steps are [b, e) (e - b >= S): a tail of tile tb from step kb (if kb > 0),
+  // whole tiles, a head of tile te up to step ke (if ke > 0).  Recomputed per piece from g, so no
+  // more than g stays live across the K loops.
+  auto bounds = [&](int& tb, int& kb, int& te, int& ke) {
+    const int64_t b = U * g / G, e = U * (g + 1) / G;
+    tb = (int)(b / S);
+    kb = (int)(b % S);
+    te = (int)(e / S);
+    ke = (int)(e % S);
+  };
+  int np;
+  {
+    int tb, kb, te, ke;
+    bounds(tb, kb, te, ke);
+    np = (ke > 0) + (te - tb - (kb > 0)) + (kb > 0);
+  }
+  // piece i in order: the head (the next workgroup waits for it), whole tiles, the tail
+  auto piece = [&](int i) -> SkPiece {
+    int tb, kb, te, ke;
+    bounds(tb, kb, te, ke);
+    const int first_full = tb + (kb > 0);
+    if (ke > 0) {
+      if (i == 0) return SkPiece{te, 0, ke};
+      --i;
+    }
+    if (i < te - first_full) return SkPiece{first_full + i, 0, S};
+    return SkPiece{tb, kb, S};
+  };
+
+  PingPong<Cfg> pp(lds);
+  int v0 = 0, t0 = 0;
+  auto start = [&](const SkPiece& p, int& pv0, int& pt0) {
+    int mt, nt;
+    group_coords<LMH_GROUP_M>(p.L, n_mt, n_nt, mt, nt);
+    pv0 = mt * Cfg::TM;
+    pt0 = nt * Cfg::TN;
+    const int kofs = p.k0 * Cfg::BK;
+    pp.start(a.weight + (int64_t)pv0 * H + kofs, H, min(Cfg::TM, a.V - pv0), a.hidden + (int64_t)pt0 * H + kofs, H,
+             min(Cfg::TN, a.T - pt0), min(H - kofs, (p.k1 - p.k0) * Cfg::BK));
+  };
+  SkPiece cur = piece(0);
+  start(cur, v0, t0);
+  bool flag_due = false;  // the head's accumulator stores are out; its flag goes up after the next K loop
+  for (int i = 0;; ++i) {
+    int y[Cfg::NSUB];
+    load_labels(a.labels, t0 + wn * Cfg::WAVE_N, lane, a.T, y);
+    f32x4 acc[MSUB][Cfg::NSUB];
+    if (cur.k0 > 0) {
+      // a tail: continue the accumulators of the previous workgroup's head
+      if (tid == 0) {
+        const int* flag = a.sk_sync + g;   // flag of workgroup g - 1
+        for (int spin = 0; spin < SK_SPIN_LIMIT && __hip_atomic_load(flag, __ATOMIC_RELAXED,
+                                                                        __HIP_MEMORY_SCOPE_AGENT) == 0; ++spin)
+          __builtin_amdgcn_s_sleep(4);
+      }
+      __syncthreads();
+      const __amdgpu_buffer_rsrc_t slot = sk_slot(a, g - 1);
+      // one offset register (the accumulator index goes in soffset), computed here from an opaque
+      // thread index so the compiler does not keep it live across the K loops
+      int voff = threadIdx.x;
+      asm volatile("" : "+v"(voff));
+      voff *= 16;
+#pragma unroll
+      for (int m = 0; m < MSUB; ++m)
+#pragma unroll
+        for (int n = 0; n < Cfg::NSUB; ++n)
+          acc[m][n] = __builtin_amdgcn_raw_buffer_load_b128(slot, voff, (m * Cfg::NSUB + n) * Cfg::NTHREADS * 16, SC1);
+      // wait for the accumulators here rather than at their first MFMA inside the K loop
+#pragma unroll
+      for (int m = 0; m < MSUB; ++m)
+#pragma unroll
+        for (int n = 0; n < Cfg::NSUB; ++n) asm volatile("" : "+v"(acc[m][n]));
+    } else {
+#pragma unroll
+      for (int m = 0; m < MSUB; ++m)
+#pragma unroll
+        for (int n = 0; n < Cfg::NSUB; ++n) acc[m][n] = (f32x4)(0.0f);
+    }
+    pp.run(acc);
+    // run() returns after every wavefront has waited for all its memory operations (vmcnt 0) and
+    // passed the loop's last barrier, so the head's accumulator stores issued before it are done
+    if (flag_due && tid == 0) __hip_atomic_store(a.sk_sync + 1 + g, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    flag_due = false;
+    const bool last = i + 1 == np;
+    if (cur.k1 < S) {
+      // a head: hand the accumulators to the next workgroup (a head is never the last piece)
+      const __amdgpu_buffer_rsrc_t slot = sk_slot(a, g);
+      int voff = threadIdx.x;
+      asm volatile("" : "+v"(voff));
+      voff *= 16;
+#pragma unroll
+      for (int m = 0; m < MSUB; ++m)
+#pragma unroll
+        for (int n = 0; n < Cfg::NSUB; ++n)
+          __builtin_amdgcn_raw_buffer_store_b128(acc[m][n], slot, voff, (m * Cfg::NSUB + n) * Cfg::NTHREADS * 16, SC1);
+      cur = piece(i + 1);
+      if (cur.k0 > 0) {
+        // the next piece is this workgroup's tail, which may wait for the previous workgroup: raise
+        // the flag now, so no chain of waits forms
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (tid == 0) __hip_atomic_store(a.sk_sync + 1 + g, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        flag_due = true;
+      }
+      start(cur, v0, t0);
+      continue;
+    }
+    int lw[Cfg::NSUB];
+    label_offsets(y, v0 + wm * WAVE_M, a, lw);
+#pragma unroll
+    for (int n = 0; n < Cfg::NSUB; ++n) asm volatile("" : "+v"(lw[n]));
+    __builtin_amdgcn_sched_barrier(0);
+    // the next piece's first loads go out before this tile's records are computed (run() returns
+    // with every slot free in every wavefront)
+    SkPiece nxt = cur;
+    int v0n = v0, t0n = t0;
+    if (!last) {
+      nxt = piece(i + 1);
+      start(nxt, v0n, t0n);
+    }
+    tile_records<Cfg, Opt>(acc, v0, t0, lw, a);
+    if (last) break;
+    cur = nxt;
+    v0 = v0n;
+    t0 = t0n;
+  }
+}
+
 // ---------------------------------------------------------------------------------------------
 // K2: fixed-order fold of the records and the final outputs
 // ---------------------------------------------------------------------------------------------
@@ -535,6 +715,12 @@ static void launch_partials_opt(const FwdArgs& a, hipStream_t stream) {
   if constexpr (Cfg::LOOP == LOOP_PINGPONG) {
     // one workgroup per CU (the tile takes all of a CU's LDS)
     const int ntiles = n_mt * n_nt;
+    if (a.sk_acc && fwd_sk_wanted(a.T, a.V, a.cus)) {
+      const int G = min(ntiles, min(a.cus, SK_MAX_WG));
+      hipLaunchKernelGGL(fwd_sk_reset_kernel, dim3(1), dim3(256), 0, stream, a.sk_sync, 1 + G);
+      hipLaunchKernelGGL((fwd_partials_sk_kernel<Cfg, Opt>), dim3(G), dim3(Cfg::NTHREADS), 0, stream, a, n_mt, n_nt);
+      return;
+    }
     hipLaunchKernelGGL(fwd_sched_reset_kernel, dim3(1), dim3(64), 0, stream, a.sched);
     hipLaunchKernelGGL((fwd_partials_persistent_kernel<Cfg, Opt>), dim3(min(ntiles, a.cus)), dim3(Cfg::NTHREADS), 0,
                        stream, a, n_mt, n_nt);
@@ -585,6 +771,18 @@ using CfgS64 = FwdCfg<PipeCfg<LMH_S64_SHAPE, LMH_S64_NS, LMH_S64_BK>, LOOP_SPREA
 // 64 < T <= 128: 256 vocab x 128 tokens, 4 wavefronts, three stages of K = 64 (144 KB of LDS).
 // Against the 256 x 256 persistent tile it wins by 13 % at T = 96 and 128 and loses from T = 192.
 using CfgMid = FwdCfg<PipeCfg<LMH_MID_SHAPE, LMH_MID_NS, 64>, LOOP_SPREAD>;
+
+bool fwd_sk_wanted(int64_t T, int64_t V, int cus) {
+  // One token tile only: with two or more, consecutive K ranges run a vocabulary tile's token tiles
+  // one after another on one workgroup instead of side by side on one XCD, and the weight is read
+  // from memory once per token tile (measured 17-27 % slower at T = 384 .. 1024).  Below T = 192
+  // the tile's steps are short enough that the hand-overs cost what the balance gains (measured:
+  // 3 % slower at T = 129, even at T = 160, 4 % faster at T = 200, 9 % at T = 256).
+  if (T < LMH_SK_MIN_T || T > 256) return false;
+  const int64_t ntiles = (V + 255) / 256;
+  const int64_t G = min(cus, SK_MAX_WG);
+  return ntiles > G && ntiles < (int64_t)LMH_SK_MAX_ROUNDS * G;
+}
 
 void launch_fwd_partials(const FwdArgs& a, hipStream_t stream) {
   if (a.T <= 32)

@@ -27,6 +27,26 @@ constexpr int BWD_SCHED_WORDS = 16;
 // Words of the forward workspace used by the large-T tile scheduler (one counter per XCD).
 constexpr int SCHED_WORDS = 16;
 
+// K-split schedule of the large-T tile for launches of few tile rounds: at most SK_MAX_WG
+// workgroups, each with one accumulator slot of a whole 256 x 256 fp32 tile in the workspace, and
+// a word array [0] = workgroup counter, [1 + g] = flag "workgroup g's accumulators are stored".
+constexpr int SK_MAX_WG = 256;
+constexpr size_t SK_SLOT_BYTES = 256 * 256 * 4;
+constexpr int SK_SYNC_WORDS = 1 + SK_MAX_WG;
+// A tail's wait for the previous workgroup ends by construction; the bound only keeps a broken
+// invariant from hanging the device.
+constexpr int SK_SPIN_LIMIT = 1 << 22;
+#ifndef LMH_SK_MAX_ROUNDS
+#define LMH_SK_MAX_ROUNDS 4
+#endif
+#ifndef LMH_SK_MIN_T
+#define LMH_SK_MIN_T 192
+#endif
+// Whether the forward of T tokens over V weight rows runs the K-split schedule when the workspace
+// has room for it: one token tile of the large-T tile (LMH_SK_MIN_T <= T <= 256), and more
+// vocabulary tiles than workgroups but fewer than LMH_SK_MAX_ROUNDS per workgroup.
+bool fwd_sk_wanted(int64_t T, int64_t V, int cus);
+
 struct FwdArgs {
   const __bf16* hidden;
   const __bf16* weight;
@@ -41,6 +61,8 @@ struct FwdArgs {
   float* zy;          // [T] label logits (divided by the temperature)
   int* sched;         // [SCHED_WORDS] tile counters, reset by the partials launch
   int* p2ok;          // [n_c] 1 if the chunk's rec2 was written by the last partials run over it
+  f32x4* sk_acc;      // [SK_MAX_WG] accumulator slots of the K-split schedule, or null (not used)
+  int* sk_sync;       // [SK_SYNC_WORDS] its workgroup counter and flags
   float* logprob;
   float* entropy;
   float* lse;

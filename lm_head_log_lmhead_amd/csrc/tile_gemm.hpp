@@ -116,11 +116,11 @@ struct TileQueue {
 // once per workgroup; the build measures where each loop landed in a first compile and sets the
 // counts (LMH_LOOP_PADS), so the placement holds whatever code precedes the loop.  Kernel ids:
 // 0-3 forward persistent (2 * temperature + sum_p2), 4-7 backward dz (2 * temperature +
-// entropy gradient), 8 gradient GEMM.
+// entropy gradient), 8 gradient GEMM, 9-12 forward K-split (2 * temperature + sum_p2).
 #ifndef LMH_LOOP_PADS
-#define LMH_LOOP_PADS 0, 0, 0, 0, 0, 0, 0, 0, 0
+#define LMH_LOOP_PADS 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0
 #endif
-constexpr int LOOP_PAD[9] = {LMH_LOOP_PADS};
+constexpr int LOOP_PAD[13] = {LMH_LOOP_PADS};
 
 template <int ID>
 __device__ __forceinline__ void loop_placement_pad() {

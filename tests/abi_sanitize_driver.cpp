@@ -35,10 +35,12 @@ int main(int argc, char** argv) {
     for (int64_t H : Hs)
       for (int64_t V : Vs) {
         const size_t fw = lmhead_logprob_fwd_workspace_size(T, H, V);
+        const size_t fw_min = lmhead_logprob_fwd_workspace_size_min(T, H, V);
         const size_t bw = lmhead_logprob_bwd_workspace_size(T, H, V);
         const bool sizes_ok = T >= 0 && T < B31 - B16 && H >= 8 && H % 8 == 0 && H <= (1 << 20) && V >= 1 &&
                               V < B31 - B16 && (T == 0 || (V + 127) / 128 <= (int64_t(1) << 36) / T);
         EXPECT((fw > 0) == sizes_ok);
+        EXPECT((fw_min > 0) == sizes_ok && fw_min <= fw);
         EXPECT((bw > 0) == sizes_ok);
         if (sizes_ok) {
           EXPECT(fw % 256 == 0 && bw % 256 == 0);
@@ -68,7 +70,14 @@ int main(int argc, char** argv) {
                  (T >= (1 << 22) ? LMH_ERR_UNSUPPORTED : LMH_ERR_HIP));
           const lmh_status_t na = lmhead_logprob_fwd_noalloc(P(0x1000), P(0x2000), I(0x3000), T, H, V, F(0x4000),
                                                              nullptr, nullptr, nullptr);
-          EXPECT(na == (fw <= LMH_NOALLOC_SCRATCH_BYTES ? LMH_ERR_HIP : LMH_ERR_WORKSPACE_TOO_SMALL));
+          EXPECT(na == (fw_min <= LMH_NOALLOC_SCRATCH_BYTES ? LMH_ERR_HIP : LMH_ERR_WORKSPACE_TOO_SMALL));
+        }
+        // the smallest forward workspace passes validation; one byte less does not
+        if (sizes_ok && T > 0 && !have_gpu) {
+          EXPECT(lmhead_logprob_fwd(P(0x1000), P(0x2000), I(0x3000), T, H, V, F(0x4000), nullptr, nullptr,
+                                    P(0x10000), fw_min - 1, nullptr) == LMH_ERR_WORKSPACE_TOO_SMALL);
+          EXPECT(lmhead_logprob_fwd(P(0x1000), P(0x2000), I(0x3000), T, H, V, F(0x4000), nullptr, nullptr,
+                                    P(0x10000), fw_min, nullptr) == LMH_ERR_HIP);
         }
         // the narrowest backward step's workspace passes validation; one byte less does not
         if (sizes_ok && T > 0 && T < (1 << 22)) {

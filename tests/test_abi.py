@@ -65,6 +65,15 @@ def test_workspace_sizes(lib):
     assert bwd >= 4096 * 16384 * 2 * 2 + 5120 * 16384 * 2 + 5120 * 4096 * 2
     # the workspace grows linearly in T for the forward
     assert lmh.lmhead_logprob_fwd_workspace_size(2 * T, H, V) > fwd
+    # few tiles per compute unit: the fast size adds the K-split schedule's accumulator slots (256 of
+    # 256 x 256 fp32) and its counter and flags; the smallest accepted size leaves them out
+    assert lmh.lmhead_logprob_fwd_workspace_size_min(T, H, V) == fwd        # 594 x 32 tiles: no split
+    for t in (192, 200, 256):                                               # 594 tiles
+        lo, hi = lmh.lmhead_logprob_fwd_workspace_size_min(t, H, V), lmh.lmhead_logprob_fwd_workspace_size(t, H, V)
+        assert hi - lo == 256 * 256 * 256 * 4 + 1280 and lo >= n_c * t * 20 + t * 4
+    for t in (1, 64, 128, 129, 191, 257, 2048):                             # below 192, or two token tiles
+        assert lmh.lmhead_logprob_fwd_workspace_size(t, H, V) == lmh.lmhead_logprob_fwd_workspace_size_min(t, H, V)
+    assert lmh.lmhead_logprob_fwd_workspace_size_min(4, 12, 10) == 0
 
 
 def _fwd(lib, hidden=16, weight=16, labels=16, T=4, H=8, V=10, logprob=16, entropy=None, lse=None,
@@ -182,7 +191,7 @@ def test_noalloc_validation_codes(lib):
         return lib.lmhead_logprob_fwd_noalloc(hidden, weight, labels, T, H, V, logprob, None, None, None)
     V = 152064
     T = 1
-    while lmh.lmhead_logprob_fwd_workspace_size(T + 1, 8, V) <= lmh.NOALLOC_SCRATCH_BYTES:
+    while lmh.lmhead_logprob_fwd_workspace_size_min(T + 1, 8, V) <= lmh.NOALLOC_SCRATCH_BYTES:
         T += 1
     assert call(T=T + 1, V=V) == lmh.LMH_ERR_WORKSPACE_TOO_SMALL
     assert call(T=1 << 30, V=V) == lmh.LMH_ERR_UNSUPPORTED             # past 2^36 record slots

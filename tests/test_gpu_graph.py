@@ -12,9 +12,10 @@ from tests.gpu_util import bits, dev, to_dev
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("T", [40, 300])
-def test_forward_and_backward_replay_in_a_graph(T):
-    H, V = 256, 3000
+# streaming tiles, the dynamic large-T schedule, and the K-split schedule (274 vocabulary tiles,
+# accumulators handed between workgroups, its counter and flags reset by a kernel in the call)
+@pytest.mark.parametrize("T,H,V", [(40, 256, 3000), (300, 256, 3000), (200, 136, 70000)])
+def test_forward_and_backward_replay_in_a_graph(T, H, V):
     print(f"[case] graph replay T={T} H={H} V={V}", flush=True)
     x = synth.make_inputs(T, H, V, seed=7, weight_std=0.05, with_grad=True)
     h, w, y, g = to_dev(x.hidden, x.weight, x.labels, x.grad)

@@ -28,15 +28,16 @@ def _problem(T, H, V, seed):
 
 
 def test_two_streams_give_the_sequential_bits():
-    # a large-T problem (persistent tiles) and a small-T one (streaming tiles)
-    problems = [_problem(300, 256, 3000, 11), _problem(40, 192, 2053, 12)]
+    # a large-T problem (persistent tiles), a small-T one (streaming tiles) and one whose forward
+    # splits the tiles' K steps between workgroups (274 tiles)
+    problems = [_problem(300, 256, 3000, 11), _problem(40, 192, 2053, 12), _problem(200, 264, 70000, 13)]
     cur = torch.cuda.current_stream()
     for run, _ in problems:
         run(cur)
     torch.cuda.synchronize()
     want = [{k: bits(v) for k, v in out.items()} for _, out in problems]
 
-    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    streams = [torch.cuda.Stream() for _ in problems]
     for rep in range(3):
         for _, out in problems:
             for t in out.values():

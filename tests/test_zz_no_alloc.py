@@ -42,7 +42,7 @@ def test_noalloc_full_vocabulary_and_limit():
     # the largest T whose workspace fits the scratch at V = 152064, then one row more is refused
     H, V = 256, 152064
     fit = 1
-    while lmh.lmhead_logprob_fwd_workspace_size(fit + 1, H, V) <= lmh.NOALLOC_SCRATCH_BYTES:
+    while lmh.lmhead_logprob_fwd_workspace_size_min(fit + 1, H, V) <= lmh.NOALLOC_SCRATCH_BYTES:
         fit += 1
     print(f"[case] noalloc at the limit: T={fit} H={H} V={V}", flush=True)
     ref, got = _pair(fit, H, V, seed=3)
