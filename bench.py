@@ -235,7 +235,12 @@ def main():
     # W (2VH bytes) streamed once for 2TVH flops: T flop/B; below the ridge the kernel is HBM-bound
     hbm_bound = T < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
     traffic = measured_traffic(a.workload)
-    kname = "fwd_partials_persistent_kernel" if T > 128 else "fwd_partials_kernel"
+    if T <= 128:
+        kname = "fwd_partials_kernel"
+    elif lmh.lmhead_logprob_fwd_workspace_size(T, H, Vp) > lmh.lmhead_logprob_fwd_workspace_size_min(T, H, Vp):
+        kname = "fwd_partials_sk_kernel"       # the K-split schedule (one token tile, few tiles per CU)
+    else:
+        kname = "fwd_partials_persistent_kernel"
     if hbm_bound:
         roof = {"bound": "hbm", "kernel": kname, "achieved": k1_gbs, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": k1_gbs / PEAK_HBM_GBS, "traffic": traffic}
