@@ -46,6 +46,11 @@
 #ifndef LMH_S64_SHAPE
 #define LMH_S64_SHAPE 1, 4, 1
 #endif
+// persistent large-T tile: tiles before the end of an XCD's range below which the next tile is
+// claimed only when the current one finishes
+#ifndef LMH_CLAIM_DEFER
+#define LMH_CLAIM_DEFER 128
+#endif
 // mid-T tile (64 < T <= LMH_MID_MAX)
 #ifndef LMH_MID_MAX
 #define LMH_MID_MAX 128
@@ -287,7 +292,13 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void fwd_partials_persistent_kernel(
   int v0 = mt * Cfg::TM, t0 = nt * Cfg::TN;
   pp.start(a.weight + (int64_t)v0 * H, H, min(Cfg::TM, a.V - v0), a.hidden + (int64_t)t0 * H, H,
            min(Cfg::TN, a.T - t0), H);
-  int claim = 0;  // thread 0: raw counter value of the next claim on this XCD's range
+  // Thread 0: raw counter value of the next tile's claim on this XCD's range, or -1 when it has
+  // not been taken yet.  A claim is taken a tile ahead while the XCD's range still has more than
+  // LMH_CLAIM_DEFER tiles past the current one; nearer the end it is taken only when the tile
+  // finishes, so the last tiles go to the workgroups that are free first.
+  int own_start, own_count;
+  xcd_range(xcd, n_mt * n_nt, own_start, own_count);
+  int claim = 0;
   if (threadIdx.x == 0) claim = q.claim(xcd);
   for (;;) {
     int y[Cfg::NSUB];
@@ -306,7 +317,10 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void fwd_partials_persistent_kernel(
     label_offsets(y, v0 + wm * WAVE_M, a, lw);
 #pragma unroll
     for (int n = 0; n < Cfg::NSUB; ++n) asm volatile("" : "+v"(lw[n]));
-    if (threadIdx.x == 0) bc[0] = q.resolve(xcd, claim);
+    if (threadIdx.x == 0) {
+      if (claim < 0) claim = q.claim(xcd);   // a deferred claim: its latency is exposed here
+      bc[0] = q.resolve(xcd, claim);
+    }
     __syncthreads();
     const int Ln = bc[0];
     __builtin_amdgcn_sched_barrier(0);
@@ -317,7 +331,7 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void fwd_partials_persistent_kernel(
       t0n = nt * Cfg::TN;
       pp.start(a.weight + (int64_t)v0n * H, H, min(Cfg::TM, a.V - v0n), a.hidden + (int64_t)t0n * H, H,
                min(Cfg::TN, a.T - t0n), H);
-      if (threadIdx.x == 0) claim = q.claim(xcd);
+      if (threadIdx.x == 0) claim = claim + LMH_CLAIM_DEFER < own_count ? q.claim(xcd) : -1;
     }
     tile_records<Cfg, Opt>(acc, v0, t0, lw, a);
     if (Ln < 0) break;
