@@ -594,8 +594,27 @@ constexpr int FIN_NSEG = 64;  // fixed number of fold segments per row
 // the state of lane s + d into its own), six dependent merges instead of a chain of 64.  Neither
 // the spread of segments over lanes nor the batching changes any value; the order is a function
 // of V only.
+// Segment states of a row block in LDS, one array per field with rows padded to TPW + 1 words:
+// the stores (consecutive lanes, consecutive tokens) and the tree's loads (consecutive lanes,
+// consecutive segments of one token, TPW + 1 words apart) hit 64 different banks.
+template <int TPW>
+struct SegStates {
+  float m[FIN_NSEG][TPW + 1], n[FIN_NSEG][TPW + 1], b[FIN_NSEG][TPW + 1], u[FIN_NSEG][TPW + 1],
+      q[FIN_NSEG][TPW + 1];
+  __device__ __forceinline__ void put(int sg, int t, const Rec& r, bool p2) {
+    m[sg][t] = r.m;
+    n[sg][t] = r.n;
+    b[sg][t] = r.b;
+    u[sg][t] = r.u;
+    if (p2) q[sg][t] = r.q;
+  }
+  __device__ __forceinline__ Rec get(int sg, int t, bool p2) const {
+    return Rec{m[sg][t], n[sg][t], b[sg][t], u[sg][t], p2 ? q[sg][t] : 0.f};
+  }
+};
+
 template <bool P2, int TPW>
-__device__ __forceinline__ void fold_row_block(const FwdArgs& a, int n_c, int blk, Rec (&part)[FIN_NSEG][TPW]) {
+__device__ __forceinline__ void fold_row_block(const FwdArgs& a, int n_c, int blk, SegStates<TPW>& part) {
   static_assert(FIN_NSEG == 64, "one segment state per lane in the tree");
   constexpr int LPT = 64 / TPW;                      // segment slots per wavefront and pass
   constexpr int PASSES = FIN_NSEG / (FIN_WAVES * LPT);
@@ -640,13 +659,13 @@ __device__ __forceinline__ void fold_row_block(const FwdArgs& a, int n_c, int bl
         seg[j] = fold<P2>(seg[j], Rec{r[j][i][0], r[j][i][1], r[j][i][2], r[j][i][3], r2[j][i]});
   }
 #pragma unroll
-  for (int j = 0; j < PASSES; ++j) part[sg[j]][tl] = seg[j];
+  for (int j = 0; j < PASSES; ++j) part.put(sg[j], tl, seg[j], P2);
   __syncthreads();
   // wavefront w merges the segment states of tokens w, w + 16, ... of the workgroup
   for (int k = w; k < TPW; k += FIN_WAVES) {
     const int tt = blk * TPW + k;
     if (tt >= T) break;  // k is the same in every lane
-    Rec st = part[lane][k];
+    Rec st = part.get(lane, k, P2);
 #pragma unroll
     for (int d = 1; d < FIN_NSEG; d *= 2) {
       Rec o;
@@ -667,7 +686,7 @@ constexpr int FIN_MAX_GRID = 1 << 16;
 
 template <bool P2, int TPW>
 __global__ __launch_bounds__(64 * FIN_WAVES) void fwd_finalize_kernel(FwdArgs a, int n_c, int nblk) {
-  __shared__ Rec part[FIN_NSEG][TPW];
+  __shared__ SegStates<TPW> part;
   for (int blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
     fold_row_block<P2, TPW>(a, n_c, blk, part);
     __syncthreads();  // the next block's segment states overwrite part
@@ -820,7 +839,7 @@ static void launch_finalize_tpw(const FwdArgs& a, int n_c, hipStream_t stream) {
 }
 
 #ifndef LMH_FINW_MAX_T
-#define LMH_FINW_MAX_T 256
+#define LMH_FINW_MAX_T 512
 #endif
 
 void launch_fwd_finalize(const FwdArgs& a, hipStream_t stream) {

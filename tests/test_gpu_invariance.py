@@ -124,7 +124,7 @@ def test_repeat_run_identity(data, reference):
 
 @pytest.mark.parametrize("tau,p2", [(1.0, False), (0.7, True)])
 def test_wave_fold_equals_block_fold(tau, p2):
-    # T <= 256 folds one wavefront per row, larger T folds in row blocks: the same rows, alone and
+    # T <= 512 folds one wavefront per row, larger T folds in row blocks: the same rows, alone and
     # inside a batch of 700, give the same bits (with a temperature and sum_p2 too)
     import lm_head_log_lmhead_amd as lmh
     H, V = 264, 20000
