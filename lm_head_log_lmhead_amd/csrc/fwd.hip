@@ -580,16 +580,16 @@ __device__ __forceinline__ void finalize_row(const FwdArgs& a, int t, const Rec&
   }
 }
 
-constexpr int FIN_WAVES = 16; // wavefronts per workgroup
 constexpr int FIN_NSEG = 64;  // fixed number of fold segments per row
 
-// A workgroup folds a block of TPW tokens at a time (TPW = 16 or 32).  Lane l of a wavefront serves
-// token l % TPW and segment slot l / TPW, so a wavefront covers 64 / TPW segments of each of its
-// tokens per pass and the 16 wavefronts cover all 64 segments in 4 TPW / 64 passes.  Small T takes
-// small TPW, so that lanes are not left idle on missing tokens; large T takes TPW = 32, which gives
-// a workgroup per CU at T = 8192.  Each segment is folded in ascending chunk order, its records
-// loaded in batches (one batch covers a segment of up to 20 chunks when TPW = 16, i.e. V up to
-// 163840); then the 64 segment states of a token are merged in a fixed binary tree inside one
+// A workgroup of FW wavefronts folds a block of TPW tokens at a time ((TPW, FW) = (8, 8), (16, 16)
+// or (32, 16)).  Lane l of a wavefront serves token l % TPW and segment slot l / TPW, so a
+// wavefront covers 64 / TPW segments of each of its tokens per pass and the FW wavefronts cover
+// all 64 segments in 64 / (FW * 64 / TPW) passes (one, or two for (32, 16)).  The block size grows
+// with T so that the blocks cover the CUs (256 of them at T = 2048, 4096 and 8192) while a
+// segment's loads stay whole 128-byte lines.  Each segment is folded in ascending chunk order, its
+// records loaded in batches (one batch covers a segment of up to 20 chunks with one pass, i.e. V
+// up to 163840); then the 64 segment states of a token are merged in a fixed binary tree inside one
 // wavefront (lane s holds segment s; at level d = 1, 2, 4, ..., 32 lane s with s % 2d == 0 merges
 // the state of lane s + d into its own), six dependent merges instead of a chain of 64.  Neither
 // the spread of segments over lanes nor the batching changes any value; the order is a function
@@ -613,11 +613,12 @@ struct SegStates {
   }
 };
 
-template <bool P2, int TPW>
+template <bool P2, int TPW, int FW>
 __device__ __forceinline__ void fold_row_block(const FwdArgs& a, int n_c, int blk, SegStates<TPW>& part) {
   static_assert(FIN_NSEG == 64, "one segment state per lane in the tree");
   constexpr int LPT = 64 / TPW;                      // segment slots per wavefront and pass
-  constexpr int PASSES = FIN_NSEG / (FIN_WAVES * LPT);
+  constexpr int PASSES = FIN_NSEG / (FW * LPT);
+  static_assert(PASSES >= 1 && PASSES * FW * LPT == FIN_NSEG, "segment slots");
   constexpr int BATCH = 20 / PASSES;                 // records per segment loaded before folding
   const int T = a.T;
   const int lane = threadIdx.x & 63;
@@ -630,7 +631,7 @@ __device__ __forceinline__ void fold_row_block(const FwdArgs& a, int n_c, int bl
   int maxlen = 0;
 #pragma unroll
   for (int j = 0; j < PASSES; ++j) {
-    sg[j] = (j * FIN_WAVES + w) * LPT + lane / TPW;
+    sg[j] = (j * FW + w) * LPT + lane / TPW;
     lo[j] = (int)((int64_t)sg[j] * n_c / FIN_NSEG);
     len[j] = (int)((int64_t)(sg[j] + 1) * n_c / FIN_NSEG) - lo[j];
     maxlen = max(maxlen, len[j]);
@@ -662,7 +663,7 @@ __device__ __forceinline__ void fold_row_block(const FwdArgs& a, int n_c, int bl
   for (int j = 0; j < PASSES; ++j) part.put(sg[j], tl, seg[j], P2);
   __syncthreads();
   // wavefront w merges the segment states of tokens w, w + 16, ... of the workgroup
-  for (int k = w; k < TPW; k += FIN_WAVES) {
+  for (int k = w; k < TPW; k += FW) {
     const int tt = blk * TPW + k;
     if (tt >= T) break;  // k is the same in every lane
     Rec st = part.get(lane, k, P2);
@@ -684,11 +685,11 @@ __device__ __forceinline__ void fold_row_block(const FwdArgs& a, int n_c, int bl
 // Grid-stride over the row blocks, so that the grid stays bounded for any T.
 constexpr int FIN_MAX_GRID = 1 << 16;
 
-template <bool P2, int TPW>
-__global__ __launch_bounds__(64 * FIN_WAVES) void fwd_finalize_kernel(FwdArgs a, int n_c, int nblk) {
+template <bool P2, int TPW, int FW>
+__global__ __launch_bounds__(64 * FW) void fwd_finalize_kernel(FwdArgs a, int n_c, int nblk) {
   __shared__ SegStates<TPW> part;
   for (int blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
-    fold_row_block<P2, TPW>(a, n_c, blk, part);
+    fold_row_block<P2, TPW, FW>(a, n_c, blk, part);
     __syncthreads();  // the next block's segment states overwrite part
   }
 }
@@ -828,14 +829,14 @@ void launch_fwd_partials(const FwdArgs& a, hipStream_t stream) {
     launch_partials_cfg<CfgBig>(a, stream);
 }
 
-template <int TPW>
+template <int TPW, int FW>
 static void launch_finalize_tpw(const FwdArgs& a, int n_c, hipStream_t stream) {
   const int nblk = (a.T + TPW - 1) / TPW;
   const dim3 grid(min(nblk, FIN_MAX_GRID));
   if (a.sum_p2)
-    hipLaunchKernelGGL((fwd_finalize_kernel<true, TPW>), grid, dim3(64 * FIN_WAVES), 0, stream, a, n_c, nblk);
+    hipLaunchKernelGGL((fwd_finalize_kernel<true, TPW, FW>), grid, dim3(64 * FW), 0, stream, a, n_c, nblk);
   else
-    hipLaunchKernelGGL((fwd_finalize_kernel<false, TPW>), grid, dim3(64 * FIN_WAVES), 0, stream, a, n_c, nblk);
+    hipLaunchKernelGGL((fwd_finalize_kernel<false, TPW, FW>), grid, dim3(64 * FW), 0, stream, a, n_c, nblk);
 }
 
 #ifndef LMH_FINW_MAX_T
@@ -852,10 +853,14 @@ void launch_fwd_finalize(const FwdArgs& a, hipStream_t stream) {
       hipLaunchKernelGGL(fwd_finalize_wave_kernel<false>, grid, dim3(64 * FINW_WAVES), 0, stream, a, n_c);
     return;
   }
-  if (a.T <= 2048)
-    launch_finalize_tpw<16>(a, n_c, stream);
+  // row blocks of TPW tokens on FW wavefronts: enough blocks to cover the CUs (256 at T = 2048,
+  // 4096 and 8192), the segment loads of a block one 128-byte line per segment or more
+  if (a.T < 4096)
+    launch_finalize_tpw<8, 8>(a, n_c, stream);
+  else if (a.T < 8192)
+    launch_finalize_tpw<16, 16>(a, n_c, stream);
   else
-    launch_finalize_tpw<32>(a, n_c, stream);
+    launch_finalize_tpw<32, 16>(a, n_c, stream);
 }
 
 }  // namespace lmh
