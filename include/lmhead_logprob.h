@@ -79,7 +79,7 @@ typedef enum {
  * vocabulary chunk), one float per row, 256 bytes of tile-scheduler counters and one int per
  * chunk.  Where the call has one 256-token tile and few 256-row vocabulary tiles per compute unit
  * (192 <= T <= 256 and 256 < ceil(V / 256) < 1024, e.g. T = 256 at V = 152064) it also holds
- * 64 MiB of accumulator slots and 1 KiB of flags, with which the partials stage splits the tiles'
+ * 64 MiB of accumulator slots and 5 KiB of flags, with which the partials stage splits the tiles'
  * K loops evenly over the compute units (same bits as without).  The initial contents do not
  * matter.
  * Calls that may run concurrently need separate workspaces. */

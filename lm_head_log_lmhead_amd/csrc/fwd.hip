@@ -361,8 +361,20 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void fwd_partials_persistent_kernel(
 // the accumulators only after it has seen the flag.  The counter and flags are zeroed by
 // fwd_sk_reset_kernel before the launch.
 
-__global__ void fwd_sk_reset_kernel(int* __restrict__ sync, int n) {
-  for (int i = threadIdx.x; i < n; i += blockDim.x) sync[i] = 0;
+// Zeroes the counter and the flags of G workgroups and writes each workgroup's range of the U K
+// steps (S per tile): [U g / G, U (g + 1) / G) as {tail tile, tail's first step, head tile, head's
+// end step}.
+__global__ void fwd_sk_reset_kernel(int* __restrict__ sync, int G, int64_t U, int S) {
+  for (int i = threadIdx.x; i <= G; i += blockDim.x) sync[i] = 0;
+  for (int g = threadIdx.x; g < G; g += blockDim.x) {
+    const int64_t b = U * g / G, e = U * (g + 1) / G;
+    int4 r;
+    r.x = (int)(b / S);
+    r.y = (int)(b % S);
+    r.z = (int)(e / S);
+    r.w = (int)(e % S);
+    reinterpret_cast<int4*>(sync + SK_BOUNDS_WORD)[g] = r;
+  }
 }
 
 struct SkPiece {
@@ -391,27 +403,15 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void fwd_partials_sk_kernel(FwdArgs 
   if (tid == 0) bc[0] = atomicAdd(a.sk_sync, 1);
   __syncthreads();
   const int g = bc[0];
-  const int64_t U = (int64_t)n_mt * n_nt * S;
-  // This workgroup's steps are [b, e) (e - b >= S): a tail of tile tb from step kb (if kb > 0),
-  // whole tiles, a head of tile te up to step ke (if ke > 0).  Recomputed per piece from g, so no
-  // more than g stays live across the K loops.
-  auto bounds = [&](int& tb, int& kb, int& te, int& ke) {
-    const int64_t b = U * g / G, e = U * (g + 1) / G;
-    tb = (int)(b / S);
-    kb = (int)(b % S);
-    te = (int)(e / S);
-    ke = (int)(e % S);
-  };
-  int np;
-  {
-    int tb, kb, te, ke;
-    bounds(tb, kb, te, ke);
-    np = (ke > 0) + (te - tb - (kb > 0)) + (kb > 0);
-  }
+  // This workgroup's steps (e - b >= S of them): a tail of tile tb from step kb (if kb > 0), whole
+  // tiles, a head of tile te up to step ke (if ke > 0), as written by fwd_sk_reset_kernel.
+  const int4 rb = reinterpret_cast<const int4*>(a.sk_sync + SK_BOUNDS_WORD)[g];
+  const int tb = __builtin_amdgcn_readfirstlane(rb.x), kb = __builtin_amdgcn_readfirstlane(rb.y);
+  const int te = __builtin_amdgcn_readfirstlane(rb.z), ke = __builtin_amdgcn_readfirstlane(rb.w);
+  const int np = (ke > 0) + (te - tb - (kb > 0)) + (kb > 0);
+  (void)G;
   // piece i in order: the head (the next workgroup waits for it), whole tiles, the tail
   auto piece = [&](int i) -> SkPiece {
-    int tb, kb, te, ke;
-    bounds(tb, kb, te, ke);
     const int first_full = tb + (kb > 0);
     if (ke > 0) {
       if (i == 0) return SkPiece{te, 0, ke};
@@ -751,7 +751,8 @@ static void launch_partials_opt(const FwdArgs& a, hipStream_t stream) {
     const int ntiles = n_mt * n_nt;
     if (a.sk_acc && fwd_sk_wanted(a.T, a.V, a.cus)) {
       const int G = min(ntiles, min(a.cus, SK_MAX_WG));
-      hipLaunchKernelGGL(fwd_sk_reset_kernel, dim3(1), dim3(256), 0, stream, a.sk_sync, 1 + G);
+      const int S = (a.H + Cfg::BK - 1) / Cfg::BK;
+      hipLaunchKernelGGL(fwd_sk_reset_kernel, dim3(1), dim3(256), 0, stream, a.sk_sync, G, (int64_t)ntiles * S, S);
       hipLaunchKernelGGL((fwd_partials_sk_kernel<Cfg, Opt>), dim3(G), dim3(Cfg::NTHREADS), 0, stream, a, n_mt, n_nt);
       return;
     }

@@ -29,10 +29,12 @@ constexpr int SCHED_WORDS = 16;
 
 // K-split schedule of the large-T tile for launches of few tile rounds: at most SK_MAX_WG
 // workgroups, each with one accumulator slot of a whole 256 x 256 fp32 tile in the workspace, and
-// a word array [0] = workgroup counter, [1 + g] = flag "workgroup g's accumulators are stored".
+// a word array [0] = workgroup counter, [1 + g] = flag "workgroup g's accumulators are stored",
+// [SK_BOUNDS_WORD + 4 g ..] = workgroup g's range of K steps.
 constexpr int SK_MAX_WG = 256;
 constexpr size_t SK_SLOT_BYTES = 256 * 256 * 4;
-constexpr int SK_SYNC_WORDS = 1 + SK_MAX_WG;
+constexpr int SK_BOUNDS_WORD = 260;  // 16-byte aligned, past the flags
+constexpr int SK_SYNC_WORDS = SK_BOUNDS_WORD + 4 * SK_MAX_WG;
 // A tail's wait for the previous workgroup ends by construction; the bound only keeps a broken
 // invariant from hanging the device.
 constexpr int SK_SPIN_LIMIT = 1 << 22;

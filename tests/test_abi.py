@@ -66,11 +66,11 @@ def test_workspace_sizes(lib):
     # the workspace grows linearly in T for the forward
     assert lmh.lmhead_logprob_fwd_workspace_size(2 * T, H, V) > fwd
     # few tiles per compute unit: the fast size adds the K-split schedule's accumulator slots (256 of
-    # 256 x 256 fp32) and its counter and flags; the smallest accepted size leaves them out
+    # 256 x 256 fp32) and its counter, flags and ranges; the smallest accepted size leaves them out
     assert lmh.lmhead_logprob_fwd_workspace_size_min(T, H, V) == fwd        # 594 x 32 tiles: no split
     for t in (192, 200, 256):                                               # 594 tiles
         lo, hi = lmh.lmhead_logprob_fwd_workspace_size_min(t, H, V), lmh.lmhead_logprob_fwd_workspace_size(t, H, V)
-        assert hi - lo == 256 * 256 * 256 * 4 + 1280 and lo >= n_c * t * 20 + t * 4
+        assert hi - lo == 256 * 256 * 256 * 4 + 5376 and lo >= n_c * t * 20 + t * 4  # slots + counter, flags, ranges
     for t in (1, 64, 128, 129, 191, 257, 2048):                             # below 192, or two token tiles
         assert lmh.lmhead_logprob_fwd_workspace_size(t, H, V) == lmh.lmhead_logprob_fwd_workspace_size_min(t, H, V)
     assert lmh.lmhead_logprob_fwd_workspace_size_min(4, 12, 10) == 0
