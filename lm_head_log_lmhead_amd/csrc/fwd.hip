@@ -358,8 +358,8 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void fwd_partials_persistent_kernel(
 // its number earlier and is running; it computes its head before anything else, so every wait
 // ends.  The hand-over uses coherent (sc1) stores and loads, which the XCDs' separate L2 caches
 // serve consistently: the writer's stores complete before it sets the flag, and the reader loads
-// the accumulators only after it has seen the flag.  The counter and flags are zeroed by
-// fwd_sk_reset_kernel before the launch.
+// the accumulators only after it has seen the flag.  The counter and flags are zeroed, and the
+// ranges written, by fwd_sk_reset_kernel before the launch.
 
 // Zeroes the counter and the flags of G workgroups and writes each workgroup's range of the U K
 // steps (S per tile): [U g / G, U (g + 1) / G) as {tail tile, tail's first step, head tile, head's
@@ -398,7 +398,6 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void fwd_partials_sk_kernel(FwdArgs 
   const int lane = tid & 63;
   const int H = a.H;
   const int S = (H + Cfg::BK - 1) / Cfg::BK;  // K steps of a tile
-  const int G = gridDim.x;
 
   if (tid == 0) bc[0] = atomicAdd(a.sk_sync, 1);
   __syncthreads();
@@ -409,7 +408,6 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void fwd_partials_sk_kernel(FwdArgs 
   const int tb = __builtin_amdgcn_readfirstlane(rb.x), kb = __builtin_amdgcn_readfirstlane(rb.y);
   const int te = __builtin_amdgcn_readfirstlane(rb.z), ke = __builtin_amdgcn_readfirstlane(rb.w);
   const int np = (ke > 0) + (te - tb - (kb > 0)) + (kb > 0);
-  (void)G;
   // piece i in order: the head (the next workgroup waits for it), whole tiles, the tail
   auto piece = [&](int i) -> SkPiece {
     const int first_full = tb + (kb > 0);
