@@ -26,8 +26,10 @@
  * sequence: one MFMA instruction shape and one K order over H, a per-row reduction inside a
  * fixed 128-column vocabulary chunk, and a fold of the chunk records in an order that depends on
  * V only.  No value is combined by atomics and nothing splits H or V by T; the only atomic
- * operations are the large-T forward's tile counters, which choose the workgroup that computes a
- * tile, never what it computes.  (Megatron-LM PR #5897
+ * operations are the persistent kernels' tile and workgroup counters and the K-split hand-over's
+ * flags, which choose the workgroup that computes a tile or part of one, never what it computes or
+ * in which order (a K-split tile's fp32 accumulators pass between workgroups exactly, continuing
+ * the same chain).  (Megatron-LM PR #5897
  * "Batch-invariant train/inference logprob parity", commit message: a row's output must not
  * change with the total row count.)
  *
