@@ -47,7 +47,7 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="fwd_T8192_H4096_V152064_peaked", choices=sorted(synth.WORKLOADS))
     p.add_argument("--cpu-sample-rows", type=int, default=-1,
                    help="rows of the workload the CPU oracle is timed on (0 disables the CPU baseline; "

@@ -41,9 +41,10 @@ FLAGS = [
     "-fno-fast-math",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # The only atomics are the persistent kernels' tile claims, issued by one thread a tile ahead
-    # of use (and the K-split's workgroup counter and flags, one thread each).  The atomic
-    # optimizer rewrites them into a wavefront-wide scan that consumes the
-    # result at once, i.e. waits (vmcnt 0) for it, and for the next tile's loads just issued.
+    # of use (near the end of a range at its end), and the K-split's workgroup counter and flags,
+    # one thread each.  The atomic optimizer rewrites them into a wavefront-wide scan that
+    # consumes the result at once, i.e. waits (vmcnt 0) for it, and for the next tile's loads
+    # just issued.
     "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wno-unused-command-line-argument",
 ]
