@@ -419,7 +419,7 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void fwd_partials_sk_kernel(FwdArgs 
     return SkPiece{tb, kb, S};
   };
 
-  PingPong<Cfg> pp(lds);
+  PingPong<Cfg, true> pp(lds);
   int v0 = 0, t0 = 0;
   auto start = [&](const SkPiece& p, int& pv0, int& pt0) {
     int mt, nt;

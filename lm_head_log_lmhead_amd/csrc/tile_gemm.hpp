@@ -363,7 +363,10 @@ __device__ __forceinline__ void tile_mainloop_spread(const __bf16* __restrict__ 
 // when run() returns no load is in flight and a persistent caller may start() its next tile at
 // once: those first loads then travel while the caller reduces the finished tile's accumulators.
 
-template <class Cfg>
+// REMAT: start() derives the lane's load positions afresh from an opaque thread index, so a caller
+// that runs several tiles with a register-heavy epilogue between them does not keep values derived
+// from them (loop-invariant to the compiler) live across that epilogue.
+template <class Cfg, bool REMAT = false>
 struct PingPong {
   static_assert(Cfg::NWAVES == 8 && Cfg::WM == 2 && Cfg::BK == 64 && Cfg::TM == 256 && Cfg::TN == 256,
                 "ping-pong loop: 8 wavefronts, 256 x 256 tile, K = 64 steps");
@@ -384,8 +387,9 @@ struct PingPong {
   uint32_t row_off, blk_stride;
   int K, nk;
 
-  __device__ __forceinline__ PingPong(char* lds_) : lds(lds_) {
-    const int tid = threadIdx.x;
+  __device__ __forceinline__ PingPong(char* lds_) : lds(lds_) { init_lane(threadIdx.x); }
+
+  __device__ __forceinline__ void init_lane(int tid) {
     lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     group = wave >> 2;
@@ -422,6 +426,11 @@ struct PingPong {
   // slot to be free: before the first tile, or after run() of the previous tile.
   __device__ __forceinline__ void start(const __bf16* __restrict__ A, int64_t lda, int rowsA,
                                         const __bf16* __restrict__ B, int64_t ldb, int rowsB, int K_) {
+    if constexpr (REMAT) {
+      int tid = threadIdx.x;
+      asm volatile("" : "+v"(tid));
+      init_lane(tid);
+    }
     desc = loads_a ? make_desc(A, (uint32_t)((int64_t)rowsA * lda * 2))
                    : make_desc(B, (uint32_t)((int64_t)rowsB * ldb * 2));
     const int64_t ld = loads_a ? lda : ldb;
