@@ -82,8 +82,11 @@ typedef enum {
  * chunk.  Where the call has one 256-token tile and few 256-row vocabulary tiles per compute unit
  * (192 <= T <= 256 and 256 < ceil(V / 256) < 1024, e.g. T = 256 at V = 152064) it also holds
  * 64 MiB of accumulator slots and 5 KiB of flags, with which the partials stage splits the tiles'
- * K loops evenly over the compute units (same bits as without).  The initial contents do not
- * matter.
+ * K loops evenly over the compute units (same bits as without); a workgroup that continues
+ * another's accumulators waits for them with a bounded poll (2^22 polls; the environment variable
+ * LMH_SK_SPIN_LIMIT can only lower the bound), and a wait that runs out, which the launch's order
+ * of workgroups rules out, makes the call's outputs NaN instead of wrong.  The initial contents do
+ * not matter.
  * Calls that may run concurrently need separate workspaces. */
 LMH_API size_t lmhead_logprob_fwd_workspace_size(int64_t T, int64_t H, int64_t V);
 

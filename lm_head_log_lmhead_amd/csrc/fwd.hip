@@ -18,6 +18,8 @@
 //    with log S = log N + log1p(B/N), and sum_p2 = Q / S^2.  (verl PR #8026, first review: fp32
 //    log_softmax over the full vocabulary then gather, with entropy and sum_pi_squared of the same
 //    softmax; SkyRL PR #1765, precision-policy commit: logprob 0 for an out-of-vocabulary label.)
+#include <stdlib.h>
+
 #include "kernels.hpp"
 
 // Build-time tuning knobs (all choices give the same bits: the per-wavefront vocabulary extent
@@ -174,7 +176,9 @@ __device__ __forceinline__ void fwd_records(f32x4 (&acc)[MSUB][NSUB], int lane, 
     if (g == 0 && tok_ok) {
       f32x4 v;
       v[0] = mx;
-      v[1] = (float)cnt;
+      // a chunk of NaN logits (max NaN, no entry equal to it) is counted once, so that the fold,
+      // which skips records of count 0, carries its NaN into the row's outputs
+      v[1] = mx == mx ? (float)cnt : 1.f;
       v[2] = b;
       v[3] = u;
       const size_t at = (size_t)chunk * (size_t)a.T + tok;
@@ -388,7 +392,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t sk_slot(const FwdArgs& a, int 
 constexpr int SC1 = 16;  // cache policy of the hand-over: coherent across the XCDs
 
 template <class Cfg, class Opt>
-__global__ __launch_bounds__(Cfg::NTHREADS) void fwd_partials_sk_kernel(FwdArgs a, int n_mt, int n_nt) {
+__global__ __launch_bounds__(Cfg::NTHREADS) void fwd_partials_sk_kernel(FwdArgs a, int n_mt, int n_nt, int spin_limit) {
   loop_placement_pad<9 + 2 * Opt::SCALED + Opt::P2>();
   __shared__ __attribute__((aligned(1024))) char lds[Cfg::LDS_BYTES];
   int* const bc = reinterpret_cast<int*>(lds + PingPong<Cfg>::B_BASE + PingPong<Cfg>::SLOT);
@@ -441,11 +445,18 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void fwd_partials_sk_kernel(FwdArgs 
       // a tail: continue the accumulators of the previous workgroup's head
       if (tid == 0) {
         const int* flag = a.sk_sync + g;   // flag of workgroup g - 1
-        for (int spin = 0; spin < SK_SPIN_LIMIT && __hip_atomic_load(flag, __ATOMIC_RELAXED,
-                                                                        __HIP_MEMORY_SCOPE_AGENT) == 0; ++spin)
+        int seen = 0;
+        for (int spin = 0; spin < spin_limit; ++spin) {
+          if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
+            seen = 1;
+            break;
+          }
           __builtin_amdgcn_s_sleep(4);
+        }
+        bc[1] = seen;  // B slot 1, which this piece's first loads leave free
       }
       __syncthreads();
+      const bool handed = __builtin_amdgcn_readfirstlane(bc[1]) != 0;
       const __amdgpu_buffer_rsrc_t slot = sk_slot(a, g - 1);
       // one offset register (the accumulator index goes in soffset), computed here from an opaque
       // thread index so the compiler does not keep it live across the K loops
@@ -462,6 +473,13 @@ __global__ __launch_bounds__(Cfg::NTHREADS) void fwd_partials_sk_kernel(FwdArgs 
       for (int m = 0; m < MSUB; ++m)
 #pragma unroll
         for (int n = 0; n < Cfg::NSUB; ++n) asm volatile("" : "+v"(acc[m][n]));
+      if (!handed) {
+        // the wait ran out: poison the tile so its records, and the rows' outputs, are NaN
+#pragma unroll
+        for (int m = 0; m < MSUB; ++m)
+#pragma unroll
+          for (int n = 0; n < Cfg::NSUB; ++n) acc[m][n] = (f32x4)(__builtin_nanf(""));
+      }
     } else {
 #pragma unroll
       for (int m = 0; m < MSUB; ++m)
@@ -751,7 +769,8 @@ static void launch_partials_opt(const FwdArgs& a, hipStream_t stream) {
       const int G = min(ntiles, min(a.cus, SK_MAX_WG));
       const int S = (a.H + Cfg::BK - 1) / Cfg::BK;
       hipLaunchKernelGGL(fwd_sk_reset_kernel, dim3(1), dim3(256), 0, stream, a.sk_sync, G, (int64_t)ntiles * S, S);
-      hipLaunchKernelGGL((fwd_partials_sk_kernel<Cfg, Opt>), dim3(G), dim3(Cfg::NTHREADS), 0, stream, a, n_mt, n_nt);
+      hipLaunchKernelGGL((fwd_partials_sk_kernel<Cfg, Opt>), dim3(G), dim3(Cfg::NTHREADS), 0, stream, a, n_mt, n_nt,
+                         sk_spin_limit());
       return;
     }
     hipLaunchKernelGGL(fwd_sched_reset_kernel, dim3(1), dim3(64), 0, stream, a.sched);
@@ -815,6 +834,13 @@ bool fwd_sk_wanted(int64_t T, int64_t V, int cus) {
   const int64_t ntiles = (V + 255) / 256;
   const int64_t G = min(cus, SK_MAX_WG);
   return ntiles > G && ntiles < (int64_t)LMH_SK_MAX_ROUNDS * G;
+}
+
+int sk_spin_limit() {
+  const char* e = getenv("LMH_SK_SPIN_LIMIT");
+  if (!e) return SK_SPIN_LIMIT;
+  const long v = strtol(e, nullptr, 10);
+  return v <= 0 ? 0 : v < SK_SPIN_LIMIT ? (int)v : SK_SPIN_LIMIT;
 }
 
 void launch_fwd_partials(const FwdArgs& a, hipStream_t stream) {

@@ -35,9 +35,13 @@ constexpr int SK_MAX_WG = 256;
 constexpr size_t SK_SLOT_BYTES = 256 * 256 * 4;
 constexpr int SK_BOUNDS_WORD = 260;  // 16-byte aligned, past the flags
 constexpr int SK_SYNC_WORDS = SK_BOUNDS_WORD + 4 * SK_MAX_WG;
-// A tail's wait for the previous workgroup ends by construction; the bound only keeps a broken
-// invariant from hanging the device.
+// A tail's wait for the previous workgroup ends by construction; the bound (polls of the flag)
+// only keeps a broken invariant from hanging the device.  A tail that gives up continues NaN
+// accumulators instead, so the call's outputs are NaN rather than wrong.
 constexpr int SK_SPIN_LIMIT = 1 << 22;
+// SK_SPIN_LIMIT, or the smaller bound the environment variable LMH_SK_SPIN_LIMIT sets (read per
+// launch; 0 makes every tail give up at once, which is how the tests take that path).
+int sk_spin_limit();
 #ifndef LMH_SK_MAX_ROUNDS
 #define LMH_SK_MAX_ROUNDS 4
 #endif

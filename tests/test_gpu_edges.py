@@ -134,3 +134,41 @@ def test_empty_batch_through_autograd():
     torch.cuda.synchronize()
     assert h.grad.shape == (0, H)
     assert torch.count_nonzero(w.grad).item() == 0
+
+
+# one token count per forward tile: 32-token, 64-token and 128-token tiles, the K-split schedule
+# (T = 200: 274 vocabulary tiles on at most 256 workgroups) and the dynamic 256 x 256 schedule
+@pytest.mark.parametrize("T", [7, 50, 100, 200, 300])
+def test_nan_inputs_reach_the_outputs(T):
+    # A NaN logit makes its row's softmax NaN (the definition's max and sum are NaN), also when a
+    # whole 128-row vocabulary chunk is NaN (no entry then equals the chunk's max); the other rows
+    # of the batch are untouched.
+    H, V = 136, 70000
+    print(f"[case] nan T={T} H={H} V={V}", flush=True)
+    x = synth.make_inputs(T, H, V, seed=T + 7)
+    wn = x.weight.clone()
+    wn[256:384] = float("nan")                       # vocabulary chunk 2, for every token
+    hn = x.hidden.clone()
+    bad_row = T // 2
+    hn[bad_row] = float("nan")                       # one token's logits, every chunk
+    for what, h_in, w_in in (("weight chunk", x.hidden, wn), ("hidden row", hn, x.weight)):
+        h, w, y = to_dev(h_in, w_in, x.labels)
+        lp, ent, lse = lmh.forward(h, w, y, entropy=True, want_lse=True)
+        torch.cuda.synchronize()
+        ref = fp64.forward(h_in, w_in, x.labels)
+        for name, got, want in (("logprob", _np(lp), ref["logprob"]), ("entropy", _np(ent), ref["entropy"]),
+                                ("lse", _np(lse), ref["lse"])):
+            assert np.array_equal(np.isnan(got), np.isnan(want)), f"{what}: NaN pattern of {name}"
+        ok = ~np.isnan(ref["lse"])
+        assert ok.sum() == (0 if what == "weight chunk" else T - 1), what
+        assert_logprob(_np(lp)[ok], ref["logprob"][ok], what)
+        assert_entropy(_np(ent)[ok], ref["entropy"][ok], what)
+    # the rows next to the NaN row have the clean batch's bits
+    h, w, y = to_dev(x.hidden, x.weight, x.labels)
+    clean = lmh.forward(h, w, y, entropy=True, want_lse=True)
+    h, w, y = to_dev(hn, x.weight, x.labels)
+    dirty = lmh.forward(h, w, y, entropy=True, want_lse=True)
+    torch.cuda.synchronize()
+    keep = np.arange(T) != bad_row
+    for c, d in zip(clean, dirty):
+        assert np.array_equal(c.cpu().view(torch.int32).numpy()[keep], d.cpu().view(torch.int32).numpy()[keep])

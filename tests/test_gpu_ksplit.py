@@ -73,3 +73,27 @@ def test_ksplit_shard():
     torch.cuda.synchronize()
     for k, t in enumerate((lp, ent, lse)):
         assert np.array_equal(bits(t), bits(one[k])), f"output {k}"
+
+
+def test_ksplit_wait_timeout_gives_nan(monkeypatch):
+    # A tail whose wait for the previous workgroup's accumulators runs out continues NaN
+    # accumulators instead of stale ones.  LMH_SK_SPIN_LIMIT=0 makes every tail give up at once:
+    # every row then folds a NaN record and all outputs are NaN (the log-prob of a label outside
+    # the vocabulary stays 0); without it the call is back to its bits.
+    T, H, V = 200, 264, 70000
+    fast = lmh.lmhead_logprob_fwd_workspace_size(T, H, V)
+    assert fast > lmh.lmhead_logprob_fwd_workspace_size_min(T, H, V), "the split applies to this shape"
+    print(f"[case] ksplit timeout T={T} H={H} V={V}", flush=True)
+    x = synth.make_inputs(T, H, V, seed=5, weight_std=0.05)
+    h, w, y = x.hidden.to(dev()), x.weight.to(dev()), x.labels.to(dev())
+    normal, _, _ = _run(h, w, y, T, H, V, 1.0, False, fast)
+    monkeypatch.setenv("LMH_SK_SPIN_LIMIT", "0")
+    _, lp, ent = _run(h, w, y, T, H, V, 1.0, False, fast)
+    monkeypatch.delenv("LMH_SK_SPIN_LIMIT")
+    lab = x.labels.numpy()
+    inv = (lab >= 0) & (lab < V)
+    lp, ent = lp.cpu().numpy(), ent.cpu().numpy()
+    assert np.isnan(ent).all(), "entropy"
+    assert np.isnan(lp[inv]).all() and (lp[~inv] == 0).all(), "logprob"
+    again, _, _ = _run(h, w, y, T, H, V, 1.0, False, fast)
+    assert np.array_equal(again, normal)
