@@ -31,16 +31,16 @@
 // small-T tiles (T <= 32 and 32 < T <= 64): wavefront grid (WM, WN, NSUB), stages and K step of
 // the spread main loop
 #ifndef LMH_SMALL_NS
-#define LMH_SMALL_NS 5
+#define LMH_SMALL_NS 3
 #endif
 #ifndef LMH_SMALL_BK
-#define LMH_SMALL_BK 64
+#define LMH_SMALL_BK 128
 #endif
 #ifndef LMH_S64_NS
 #define LMH_S64_NS 3
 #endif
 #ifndef LMH_S64_BK
-#define LMH_S64_BK 64
+#define LMH_S64_BK 128
 #endif
 #ifndef LMH_SMALL_SHAPE
 #define LMH_SMALL_SHAPE 1, 2, 1
@@ -813,11 +813,14 @@ using CfgBig = FwdCfg<PipeCfg<2, 4, 4, 2, 64>, LOOP_PINGPONG>;
 // They cover 128 vocabulary rows (one wavefront's extent), so the 1188 tiles of V = 152064 give
 // 4.6 tiles per CU and the last round of tiles leaves few CUs idle (256-row tiles gave 2.3 per CU
 // and ran 10 % longer); one workgroup per CU holds enough loads in flight.
-// T <= 32: 128 vocab x 32 tokens, 2 wavefronts (16 tokens each), five stages of K = 64 with the
-// loads spread between the MFMAs (100 KB of LDS)
+// T <= 32: 128 vocab x 32 tokens, 2 wavefronts (16 tokens each), three stages of K = 128 with the
+// loads spread between the MFMAs (120 KB of LDS).  A K step of 128 reads 256 contiguous bytes of
+// each weight row: 0.7-1.5 % faster at T = 16 and 32 than five stages of K = 64 (four stages of
+// K = 128 were slower).
 using CfgSmall = FwdCfg<PipeCfg<LMH_SMALL_SHAPE, LMH_SMALL_NS, LMH_SMALL_BK>, LOOP_SPREAD>;
-// 32 < T <= 64: 128 vocab x 64 tokens, 4 wavefronts (16 tokens each), three stages of K = 64
-// (72 KB of LDS, so two workgroups share a CU: 1.5 % faster at T = 64 than four stages, one per CU)
+// 32 < T <= 64: 128 vocab x 64 tokens, 4 wavefronts (16 tokens each), three stages of K = 128
+// (144 KB of LDS, one workgroup per CU): 0.5 % faster at T = 48 and 64 than three stages of K = 64
+// with two workgroups per CU, which had been 1.5 % faster than four stages of K = 64.
 using CfgS64 = FwdCfg<PipeCfg<LMH_S64_SHAPE, LMH_S64_NS, LMH_S64_BK>, LOOP_SPREAD>;
 
 // 64 < T <= 128: 256 vocab x 128 tokens, 4 wavefronts, three stages of K = 64 (144 KB of LDS).

@@ -150,12 +150,15 @@ struct PipeCfg {
   static constexpr int B_IPW = TN / RPI / NWAVES;
   static constexpr int STAGE_BYTES = (TM + TN) * ROW;
   static constexpr int LDS_BYTES = NS * STAGE_BYTES;
-  static_assert(BK == 32 || BK == 64, "BK");
+  static_assert(BK == 32 || BK == 64 || BK == 128, "BK");
   static_assert(TM % (RPI * NWAVES) == 0 && TN % (RPI * NWAVES) == 0 && B_IPW >= 1, "DMA split");
   static_assert(NS >= 2 && (NS - 1) * (A_IPW + B_IPW) <= 63, "vmcnt range");
-  // Conflict-free ds_read_b128 of 16 consecutive rows at one logical chunk: BK = 64 rows are
-  // 128 B (two per 256-byte bank line), BK = 32 rows are 64 B (four per line).
-  __device__ static __forceinline__ int swz(int r) { return BK == 64 ? (r >> 1) & 7 : (r >> 2) & 3; }
+  // Conflict-free ds_read_b128 of 16 consecutive rows at one logical chunk: BK = 128 rows are
+  // 256 B (one 256-byte bank line each), BK = 64 rows 128 B (two per line), BK = 32 rows 64 B
+  // (four per line).
+  __device__ static __forceinline__ int swz(int r) {
+    return BK == 128 ? r & 15 : BK == 64 ? (r >> 1) & 7 : (r >> 2) & 3;
+  }
   // byte offset inside a row of lane `lane`'s fragment chunk for k-slice s (fsw = swz(lane % 16))
   __device__ static __forceinline__ int koff(int s, int lane, int fsw) { return ((4 * s + (lane >> 4)) ^ fsw) << 4; }
 };
