@@ -842,7 +842,9 @@ bool fwd_sk_wanted(int64_t T, int64_t V, int cus) {
 int sk_spin_limit() {
   const char* e = getenv("LMH_SK_SPIN_LIMIT");
   if (!e) return SK_SPIN_LIMIT;
-  const long v = strtol(e, nullptr, 10);
+  char* end = nullptr;
+  const long v = strtol(e, &end, 10);
+  if (end == e) return SK_SPIN_LIMIT;  // not a number: the default bound
   return v <= 0 ? 0 : v < SK_SPIN_LIMIT ? (int)v : SK_SPIN_LIMIT;
 }
 
