@@ -55,6 +55,9 @@ def parse():
     p.add_argument("--bwd-workspace-mb", type=int, default=0,
                    help="run the backward with a workspace of this many MiB (0: the size of the fastest "
                         "schedule); the library then takes the widest vocabulary step that fits")
+    p.add_argument("--fwd-workspace", choices=("fast", "min"), default="fast",
+                   help="forward workspace: the size of the fastest schedule, or the smallest accepted "
+                        "(no K-split accumulator slots: the dynamic whole-tile schedule everywhere)")
     p.add_argument("--copy-bytes", type=int, default=0,
                    help="also run a plain device copy of this many bytes (counter calibration)")
     return p.parse_args()
@@ -157,7 +160,9 @@ def main():
     ent = torch.empty(T, dtype=torch.float32, device=dev) if (wl.entropy or wl.entropy_grad) else None
     lse = torch.empty(T, dtype=torch.float32, device=dev)
     p2 = torch.empty(T, dtype=torch.float32, device=dev) if wl.sum_p2 else None
-    ws = torch.empty(lmh.lmhead_logprob_fwd_workspace_size(T, H, V), dtype=torch.uint8, device=dev)
+    ws_size = (lmh.lmhead_logprob_fwd_workspace_size if a.fwd_workspace == "fast"
+               else lmh.lmhead_logprob_fwd_workspace_size_min)
+    ws = torch.empty(ws_size(T, H, V), dtype=torch.uint8, device=dev)
     # vocabulary shards: the step runs shard 0's partials, then the fold over every shard's records
     shards = synth.shard_bounds(V, wl.shards)
     v0, v1 = shards[0]
@@ -234,10 +239,11 @@ def main():
     k1_gbs = alg_bytes / (k1 * 1e-3) / 1e9
     # W (2VH bytes) streamed once for 2TVH flops: T flop/B; below the ridge the kernel is HBM-bound
     hbm_bound = T < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
-    traffic = measured_traffic(a.workload)
+    traffic = measured_traffic(a.workload) if a.fwd_workspace == "fast" else None
     if T <= 128:
         kname = "fwd_partials_kernel"
-    elif lmh.lmhead_logprob_fwd_workspace_size(T, H, Vp) > lmh.lmhead_logprob_fwd_workspace_size_min(T, H, Vp):
+    elif (a.fwd_workspace == "fast"
+          and lmh.lmhead_logprob_fwd_workspace_size(T, H, Vp) > lmh.lmhead_logprob_fwd_workspace_size_min(T, H, Vp)):
         kname = "fwd_partials_sk_kernel"       # the K-split schedule (one token tile, few tiles per CU)
     else:
         kname = "fwd_partials_persistent_kernel"
@@ -267,6 +273,7 @@ def main():
                    **({"temperature": tau} if tau != 1.0 else {}), **({"sum_p2": True} if wl.sum_p2 else {}),
                    **({"entropy_grad": True} if wl.entropy_grad else {}),
                    **({"bwd_workspace_bytes": wsb_bytes} if wl.backward else {}),
+                   **({"fwd_workspace": "min"} if a.fwd_workspace == "min" else {}),
                    **({"vocab_shard": [v0, v1], "shards": wl.shards} if wl.shards > 1 else {})},
         "tflops": flops / (ms * 1e-3) / 1e12,
         "pct_bf16_mfma_peak": 100.0 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
