@@ -97,3 +97,8 @@ def test_ksplit_wait_timeout_gives_nan(monkeypatch):
     assert np.isnan(lp[inv]).all() and (lp[~inv] == 0).all(), "logprob"
     again, _, _ = _run(h, w, y, T, H, V, 1.0, False, fast)
     assert np.array_equal(again, normal)
+    # a value that is not a number keeps the default bound
+    monkeypatch.setenv("LMH_SK_SPIN_LIMIT", "none")
+    other, _, _ = _run(h, w, y, T, H, V, 1.0, False, fast)
+    monkeypatch.delenv("LMH_SK_SPIN_LIMIT")
+    assert np.array_equal(other, normal)
